@@ -1,0 +1,65 @@
+"""Paged NVFP4 KV cache, oracle side (test infrastructure; see the package docstring).
+
+The cache writer quantizes bf16 K/V vectors, chooses block scales, packs the
+codes and maps the result into paged cache slots ("NVFP4 KV cache prefill vs
+decode performance", section "NVFP4 stores 4.5 bits per value before
+padding"; "NVFP4 KV cache vs NVFP4 weights", section "The cache quantizes
+values during serving").  The block-scale plane is kept linear (row-major,
+not swizzled), as the FP4 utility kernels of "NVFP4 KV cache A4Q prefill
+explained", section "Preserve the capacity and decode case" use it.
+
+Page layout (a reading; the pages fix no layout), per layer and for X in {K, V}:
+
+* ``X_data [num_pages][num_kv_heads][page_size][head_dim / 2]`` uint8
+* ``X_scale[num_pages][num_kv_heads][page_size][head_dim / 16]`` uint8
+
+A slot is ``page * page_size + offset``; slots < 0 are skipped.  Slots within
+one append call are assumed distinct.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codec
+
+
+class PagedCache:
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int = 128,
+                 page_size: int = 16, k_global: float = 1.0, v_global: float = 1.0):
+        shape_d = (num_pages, num_kv_heads, page_size, head_dim // 2)
+        shape_s = (num_pages, num_kv_heads, page_size, head_dim // codec.BLOCK)
+        self.k_data = np.zeros(shape_d, np.uint8)
+        self.v_data = np.zeros(shape_d, np.uint8)
+        self.k_scale = np.zeros(shape_s, np.uint8)
+        self.v_scale = np.zeros(shape_s, np.uint8)
+        self.num_pages, self.num_kv_heads = num_pages, num_kv_heads
+        self.head_dim, self.page_size = head_dim, page_size
+        self.k_global, self.v_global = float(k_global), float(v_global)
+
+    def nbytes(self) -> int:
+        return sum(a.nbytes for a in (self.k_data, self.v_data, self.k_scale, self.v_scale))
+
+    def append(self, k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray):
+        """Quantize bf16 K/V ``[T][num_kv_heads][head_dim]`` and write them to their slots."""
+        slots = np.asarray(slot_mapping, dtype=np.int64)
+        keep = slots >= 0
+        page = slots[keep] // self.page_size
+        off = slots[keep] % self.page_size
+        for bits, data, scale, g in ((k_bits, self.k_data, self.k_scale, self.k_global),
+                                     (v_bits, self.v_data, self.v_scale, self.v_global)):
+            codes, sc = codec.quantize(codec.bf16_to_f32(bits), g)
+            data[page, :, off, :] = codec.pack(codes)[keep]
+            scale[page, :, off, :] = sc[keep]
+
+    def token_rows(self, pages: np.ndarray, offsets: np.ndarray):
+        """Packed rows and scale codes of the given (page, offset) tokens:
+        (k_data, k_scale, v_data, v_scale), each [n][num_kv_heads][...]."""
+        return (self.k_data[pages, :, offsets, :], self.k_scale[pages, :, offsets, :],
+                self.v_data[pages, :, offsets, :], self.v_scale[pages, :, offsets, :])
+
+    def gather(self, block_table_row: np.ndarray, n: int):
+        """Dequantized K and V of positions 0..n-1 of one sequence: float64 [n][H][D]."""
+        pos = np.arange(n)
+        pages = np.asarray(block_table_row, dtype=np.int64)[pos // self.page_size]
+        kd, ks, vd, vs = self.token_rows(pages, pos % self.page_size)
+        return (codec.dequantize(kd, ks, self.k_global), codec.dequantize(vd, vs, self.v_global))

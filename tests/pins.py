@@ -1,0 +1,226 @@
+"""Checks that tie the oracle to facts outside itself.
+
+Each check raises AssertionError when the oracle disagrees with what the
+pages print, with a format definition, with exact rational arithmetic, or
+with brute force.  The CPU tests run them on the oracle as it is, and run
+some of them again on copies of the oracle with a planted mistake, to show
+that each pin would catch that mistake.
+"""
+from __future__ import annotations
+
+import bisect
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def finite_bf16_patterns() -> np.ndarray:
+    """Every finite bfloat16 bit pattern (both signs, both zeros): 65,280 values."""
+    p = np.arange(65536, dtype=np.uint32)
+    finite = ((p >> 7) & 0xFF) != 0xFF
+    return p[finite].astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------------------------------
+# Formats
+# ---------------------------------------------------------------------------------------
+
+E2M1_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def check_e2m1_grid(codec):
+    vals = codec.e2m1_value(np.arange(16))
+    assert list(vals[:8]) == E2M1_GRID, vals[:8]
+    assert list(-vals[8:]) == E2M1_GRID, vals[8:]
+    assert np.signbit(vals[8]) and not np.signbit(vals[0])
+
+
+def check_e4m3_values(codec):
+    """Fixed points of the E4M3FN definition: bias 7, 2^-9 smallest subnormal,
+    2^-6 smallest normal, 448 largest, 0x7F NaN, strictly increasing codes."""
+    v = codec.e4m3_value(np.arange(256))
+    assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x39] == 1.125
+    assert v[0x7E] == 448.0 and math.isnan(v[0x7F]) and math.isnan(v[0xFF])
+    assert v[0x80 | 0x38] == -1.0
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0) and len(pos) == 127
+
+
+def _fraction_e4m3_table():
+    out = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        out.append(Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return out
+
+
+def expected_scale_code(amax: Fraction, table=None) -> int:
+    """Exact E4M3 rounding (nearest, ties to even code, saturating) of amax/6."""
+    table = table or _fraction_e4m3_table()
+    q = amax / 6
+    if q >= table[-1]:
+        return 126
+    i = bisect.bisect_left(table, q)
+    if table[i] == q:
+        return i
+    lo, hi = i - 1, i
+    dl, dh = q - table[lo], table[hi] - q
+    if dl < dh:
+        return lo
+    if dh < dl:
+        return hi
+    return lo if lo % 2 == 0 else hi
+
+
+def check_scale_rounding_exhaustive(codec):
+    """Every positive finite bf16 amax, against exact rational rounding of amax/6."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    amax = bf16_value(bits)
+    blocks = np.zeros((len(bits), 16), np.float32)
+    blocks[:, 5] = amax
+    got = codec.block_scale_codes(blocks)[:, 0]
+    table = _fraction_e4m3_table()
+    exp = np.array([expected_scale_code(Fraction(float(a)), table) for a in amax], np.uint8)
+    bad = np.nonzero(got != exp)[0]
+    assert len(bad) == 0, f"{len(bad)} mismatches, first amax={amax[bad[0]]!r} got {got[bad[0]]} want {exp[bad[0]]}"
+
+
+def threshold_code(y: np.ndarray, s: float) -> np.ndarray:
+    """E2M1 code from comparisons against exact midpoints t*s (ties to the even code)."""
+    a = np.abs(y.astype(np.float64))
+    mag = ((a > 0.25 * s).astype(np.int64) + (a >= 0.75 * s) + (a > 1.25 * s) + (a >= 1.75 * s)
+           + (a > 2.5 * s) + (a >= 3.5 * s) + (a > 5.0 * s))
+    if s == 0:
+        mag = np.zeros_like(mag)
+    return ((np.signbit(y).astype(np.int64) << 3) | mag).astype(np.uint8)
+
+
+def check_element_rounding_exhaustive(codec, scale_codes=range(0, 127)):
+    """All finite bf16 values (both signs) under every E4M3 scale, against the threshold form."""
+    y = bf16_value(finite_bf16_patterns())
+    for c in scale_codes:
+        s = float(codec.e4m3_value(c))
+        got = codec.e2m1_encode(y.astype(np.float64), s)
+        exp = threshold_code(y, s)
+        bad = np.nonzero(got != exp)[0]
+        assert len(bad) == 0, f"scale code {c:#x}: {len(bad)} mismatches, first y={y[bad[0]]!r}"
+
+
+def check_worked_block(codec):
+    g = golden("worked_block.json")
+    x = np.array(g["values"], np.float32)
+    codes, sc = codec.quantize(x)
+    assert int(sc[0]) == int(g["scale_code"], 16)
+    assert [int(c) for c in codes] == [int(c, 16) for c in g["element_codes"]]
+    assert codec.pack(codes).tobytes().hex() == g["packed_hex"]
+    assert list(codec.dequantize(codec.pack(codes), sc)) == g["dequantized"]
+
+
+# ---------------------------------------------------------------------------------------
+# Footprint figures printed on the pages
+# ---------------------------------------------------------------------------------------
+
+def check_footprint(cache_mod):
+    g = golden("footprint.json")
+    one = cache_mod.PagedCache(num_pages=1, num_kv_heads=1, head_dim=128, page_size=16)
+    per_token_head_x = one.nbytes() // 16 // 2  # bytes per (token, head) for one of K or V
+    bits_per_block = per_token_head_x * 8 // (128 // 16)
+    assert bits_per_block == g["bits_per_block_of_16"]["value"]
+    assert bits_per_block / 16 == g["bits_per_value"]["value"]
+    ratio = (bits_per_block / 16) / 8
+    assert ratio == g["ratio_to_fp8"]["value"]
+    assert round(1 / ratio, 2) == g["capacity_multiplier_rounded"]["value"]
+
+    h8 = cache_mod.PagedCache(num_pages=1, num_kv_heads=8, head_dim=128, page_size=16)
+    per_token_layer = h8.nbytes() // 16
+    fp8_64 = 2 * 64 * 8 * 128
+    assert fp8_64 == g["fp8_bytes_per_token_L64_H8_D128"]["value"]
+    assert per_token_layer * 64 == g["nvfp4_bytes_per_token_L64_H8_D128"]["value"]
+    assert 131072 * fp8_64 == g["fp8_gib_at_131072_tokens"]["value"] * 2 ** 30
+    assert 131072 * per_token_layer * 64 == g["nvfp4_gib_at_131072_tokens"]["value"] * 2 ** 30
+    vals80 = 2 * 80 * 8 * 128
+    assert vals80 == g["values_per_token_L80_H8_D128"]["value"]
+    assert vals80 * 2 == g["bf16_bytes_per_token_L80"]["value"]
+    assert vals80 == g["fp8_kib_per_token_L80"]["value"] * 1024
+    nv80 = per_token_layer * 80
+    assert nv80 == g["nvfp4_bytes_per_token_L80"]["value"]
+    assert round(32768 * nv80 / 2 ** 30, 2) == g["nvfp4_gib_32768_tokens_L80_about"]["value"]
+    assert 32768 * vals80 * 2 == g["bf16_gib_32768_tokens_L80"]["value"] * 2 ** 30
+    assert 32768 * vals80 == g["fp8_gib_32768_tokens_L80"]["value"] * 2 ** 30
+    assert round(8 * 32768 * nv80 / 2 ** 30, 1) == g["nvfp4_gib_8_seqs_about"]["value"]
+    assert 8 * 32768 * vals80 * 2 == g["bf16_gib_8_seqs"]["value"] * 2 ** 30
+
+
+# ---------------------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------------------
+
+def brute_force_attention(q, k, v, last_visible, sm_scale):
+    """Python-float loops: z, max, exp, sum and the weighted sum of V, row by row."""
+    n, d = len(q), len(q[0])
+    out, lses = [], []
+    for i in range(n):
+        z = []
+        for j in range(last_visible[i] + 1):
+            z.append(sm_scale * math.fsum(float(q[i][t]) * float(k[j][t]) for t in range(d)))
+        m = max(z)
+        e = [math.exp(x - m) for x in z]
+        den = math.fsum(e)
+        out.append([math.fsum(e[j] * float(v[j][t]) for j in range(len(e))) / den for t in range(d)])
+        lses.append(m + math.log(den))
+    return np.array(out), np.array(lses)
+
+
+def check_attention_bruteforce(codec, cache_mod, attention, seed=7, head_dim=32):
+    """Tiny ragged shapes, all rows, GQA 2, vs Python loops over independently dequantized K/V."""
+    rng = np.random.default_rng(seed)
+    q_lens, kv_lens = [1, 3, 5], [1, 7, 9]
+    hq, hkv, ps = 4, 2, 16
+    pages = [(n + ps - 1) // ps for n in kv_lens]
+    perm = rng.permutation(sum(pages) + 2)
+    bt = np.zeros((len(kv_lens), max(pages)), np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[off:off + n]; off += n
+    cache = cache_mod.PagedCache(sum(pages) + 2, hkv, head_dim=head_dim, page_size=ps)
+    sm = 1 / math.sqrt(head_dim)
+    qs, ks, vs = [], [], []
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        k = (rng.standard_normal((kl, hkv, head_dim)) * 2).astype(np.float32)
+        v = rng.standard_normal((kl, hkv, head_dim)).astype(np.float32)
+        kb = (k.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 input will do
+        vb = (v.view(np.uint32) >> 16).astype(np.uint16)
+        pos = np.arange(kl)
+        slots = bt[b][pos // ps].astype(np.int64) * ps + pos % ps
+        cache.append(kb, vb, slots)
+        qs.append((rng.standard_normal((ql, hq, head_dim)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+        ks.append(kb); vs.append(vb)
+    qb = np.concatenate(qs)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    o, lse = attention.prefill(cache, qb, cu, kv_lens, bt, sm)
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        for kvh in range(hkv):
+            kc, ksc = codec.quantize(bf16_value(ks[b][:, kvh]))
+            vc, vsc = codec.quantize(bf16_value(vs[b][:, kvh]))
+            kd = codec.dequantize(codec.pack(kc), ksc)
+            vd = codec.dequantize(codec.pack(vc), vsc)
+            for h in range(kvh * (hq // hkv), (kvh + 1) * (hq // hkv)):
+                qv = bf16_value(qs[b][:, h]).astype(np.float64)
+                ref_o, ref_l = brute_force_attention(qv, kd, vd, [kl - ql + i for i in range(ql)], sm)
+                np.testing.assert_allclose(o[cu[b]:cu[b + 1], h], ref_o, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(lse[cu[b]:cu[b + 1], h], ref_l, rtol=0, atol=1e-12)
