@@ -1,0 +1,187 @@
+"""Thin ctypes binding over ``libnvfp4kv.so`` (argument marshalling only).
+
+Every step of the path runs in the HIP library; this module only checks tensor
+dtypes/devices, passes device pointers and the current HIP stream, and allocates
+the workspace tensors the C ABI asks for.  If the library is missing it raises:
+there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+
+_ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+
+class Nvfp4KVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("k_data", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_data", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_global", ctypes.c_float), ("v_global", ctypes.c_float),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    C = ctypes.POINTER(CacheDesc)
+    lib.nvfp4_kv_append.argtypes = [C, P, P, I64, I64, P, I32, P]
+    lib.nvfp4_kv_append.restype = ctypes.c_int
+    lib.paged_prefill_nvfp4_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
+    lib.paged_prefill_nvfp4_workspace_size.restype = SZ
+    lib.paged_prefill_nvfp4.argtypes = [C, P, P, P, P, I32, I32, I32, I32, I32, I32, F, I32, P, I32,
+                                        P, I32, P, SZ, P]
+    lib.paged_prefill_nvfp4.restype = ctypes.c_int
+    lib.paged_decode_nvfp4_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.paged_decode_nvfp4_workspace_size.restype = SZ
+    lib.paged_decode_nvfp4.argtypes = [C, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P]
+    lib.paged_decode_nvfp4.restype = ctypes.c_int
+    lib.nvfp4kv_last_error.argtypes = []
+    lib.nvfp4kv_last_error.restype = ctypes.c_char_p
+    lib.nvfp4kv_version.argtypes = []
+    lib.nvfp4kv_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Nvfp4KVError(rc, load_library().nvfp4kv_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class NVFP4KVCache:
+    """Device memory of one layer's paged NVFP4 cache (allocated with torch, zero-filled)."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, device="cuda", k_global: float = 1.0,
+                 v_global: float = 1.0):
+        shape_d = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM // 2)
+        shape_s = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM // 16)
+        z = lambda s: torch.zeros(s, dtype=torch.uint8, device=device)  # noqa: E731
+        self.k_data, self.k_scale = z(shape_d), z(shape_s)
+        self.v_data, self.v_scale = z(shape_d), z(shape_s)
+        self.num_pages, self.num_kv_heads = num_pages, num_kv_heads
+        self.k_global, self.v_global = float(k_global), float(v_global)
+
+    def desc(self) -> CacheDesc:
+        return CacheDesc(self.k_data.data_ptr(), self.k_scale.data_ptr(), self.v_data.data_ptr(),
+                         self.v_scale.data_ptr(), self.k_global, self.v_global, self.num_pages,
+                         PAGE_SIZE, self.num_kv_heads, HEAD_DIM)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.k_data, self.k_scale, self.v_data, self.v_scale))
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} CUDA tensor")
+
+
+def append(cache: NVFP4KVCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor):
+    """nvfp4_kv_append: k, v bf16 [T][Hkv][128] (head/dim contiguous); slot_mapping int64 [T]."""
+    _need(k, torch.bfloat16, "k"); _need(v, torch.bfloat16, "v")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (cache.num_kv_heads, HEAD_DIM):
+        raise ValueError(f"k/v must be [T][{cache.num_kv_heads}][{HEAD_DIM}]")
+    if k.stride(2) != 1 or k.stride(1) != HEAD_DIM or v.stride(2) != 1 or v.stride(1) != HEAD_DIM:
+        raise ValueError("k/v heads and head dims must be contiguous")
+    if not slot_mapping.is_contiguous() or slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must be contiguous with one slot per token")
+    d = cache.desc()
+    _check(load_library().nvfp4_kv_append(ctypes.byref(d), k.data_ptr(), v.data_ptr(), k.stride(0),
+                                          v.stride(0), slot_mapping.data_ptr(), k.shape[0],
+                                          _stream()))
+
+
+def prefill_workspace_size(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,
+                           num_splits=0) -> int:
+    return load_library().paged_prefill_nvfp4_workspace_size(batch, total_q, max_q_len, max_kv_len,
+                                                            num_qo_heads, num_kv_heads, HEAD_DIM,
+                                                            num_splits)
+
+
+def prefill(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+            kv_lens: torch.Tensor, block_table: torch.Tensor, max_q_len: int, max_kv_len: int,
+            sm_scale: float, causal: bool = True, out: torch.Tensor | None = None,
+            out_dtype=torch.bfloat16, return_lse: bool = False, num_splits: int = 0,
+            workspace: torch.Tensor | None = None):
+    """paged_prefill_nvfp4: q bf16 [total_q][Hq][128]; returns out (and lse if asked)."""
+    _need(q, torch.bfloat16, "q"); _need(cu_seqlens_q, torch.int32, "cu_seqlens_q")
+    _need(kv_lens, torch.int32, "kv_lens"); _need(block_table, torch.int32, "block_table")
+    if not q.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("q and block_table must be contiguous")
+    total_q, hq = q.shape[0], q.shape[1]
+    batch = kv_lens.numel()
+    if out is None:
+        out = torch.empty((total_q, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    ws_bytes = prefill_workspace_size(batch, total_q, max_q_len, max_kv_len, hq, cache.num_kv_heads,
+                                      num_splits)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    d = cache.desc()
+    _check(load_library().paged_prefill_nvfp4(
+        ctypes.byref(d), q.data_ptr(), cu_seqlens_q.data_ptr(), kv_lens.data_ptr(),
+        block_table.data_ptr(), block_table.shape[1], batch, total_q, max_q_len, max_kv_len, hq,
+        sm_scale, 1 if causal else 0, out.data_ptr(), 1 if out.dtype == torch.float32 else 0,
+        _ptr(lse), num_splits, _ptr(workspace) if ws_bytes else None, ws_bytes, _stream()))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_size(batch, max_kv_len, num_qo_heads, num_kv_heads, num_splits=0) -> int:
+    return load_library().paged_decode_nvfp4_workspace_size(batch, max_kv_len, num_qo_heads,
+                                                           num_kv_heads, HEAD_DIM, num_splits)
+
+
+def decode(cache: NVFP4KVCache, q: torch.Tensor, kv_lens: torch.Tensor, block_table: torch.Tensor,
+           max_kv_len: int, sm_scale: float, out: torch.Tensor | None = None,
+           out_dtype=torch.bfloat16, return_lse: bool = False, num_splits: int = 0,
+           workspace: torch.Tensor | None = None):
+    """paged_decode_nvfp4: q bf16 [B][Hq][128]; returns out (and lse if asked)."""
+    _need(q, torch.bfloat16, "q"); _need(kv_lens, torch.int32, "kv_lens")
+    _need(block_table, torch.int32, "block_table")
+    if not q.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("q and block_table must be contiguous")
+    batch, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((batch, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    ws_bytes = decode_workspace_size(batch, max_kv_len, hq, cache.num_kv_heads, num_splits)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    d = cache.desc()
+    _check(load_library().paged_decode_nvfp4(
+        ctypes.byref(d), q.data_ptr(), kv_lens.data_ptr(), block_table.data_ptr(),
+        block_table.shape[1], batch, max_kv_len, hq, sm_scale, out.data_ptr(),
+        1 if out.dtype == torch.float32 else 0, _ptr(lse), num_splits, workspace.data_ptr(),
+        workspace.numel(), _stream()))
+    return (out, lse) if return_lse else out

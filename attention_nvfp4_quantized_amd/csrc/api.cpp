@@ -1,0 +1,310 @@
+// C ABI of the NVFP4 paged KV-cache attention library: argument validation, grid and split
+// sizing, and kernel launches.  Nothing here allocates, frees or synchronizes.
+#include "../../include/nvfp4kv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernel_params.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return NVFP4KV_OK;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(NVFP4KV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_cache(const nvfp4kv_cache_t* c) {
+  if (!c) return fail(NVFP4KV_EINVAL, "cache descriptor is NULL");
+  if (!c->k_data || !c->k_scale || !c->v_data || !c->v_scale)
+    return fail(NVFP4KV_EINVAL, "cache plane pointer is NULL");
+  if (c->head_dim != 128)
+    return fail(NVFP4KV_EUNSUPPORTED, "head_dim %d unsupported (K and V head size must be 128)",
+                c->head_dim);
+  if (c->page_size != 16) return fail(NVFP4KV_EUNSUPPORTED, "page_size %d unsupported (16)", c->page_size);
+  if (c->num_kv_heads < 1) return fail(NVFP4KV_EINVAL, "num_kv_heads must be >= 1");
+  if (c->num_pages < 1) return fail(NVFP4KV_EINVAL, "num_pages must be >= 1");
+  if (!(c->k_global > 0.0f) || !std::isfinite(c->k_global) || !(c->v_global > 0.0f) ||
+      !std::isfinite(c->v_global))
+    return fail(NVFP4KV_EINVAL, "global scales must be finite and > 0");
+  return NVFP4KV_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kDecodeChunkMin = 512;  // keys per decode slice, lower bound
+
+// Waves per prefill workgroup: 8 when the query tile is long enough, else the fewest 32-column
+// waves that hold every (row, head) column of the longest sequence.
+int prefill_waves(int max_q_len, int group) {
+  const long cols = (long)max_q_len * group;
+  if (cols >= 256) return 8;
+  if (cols > 64) return 4;
+  if (cols > 32) return 2;
+  return 1;
+}
+
+int prefill_splits(int batch, int q_tiles, int num_kv_heads, int max_kv_len, int requested) {
+  if (requested > 0) return requested;
+  const long base = (long)batch * q_tiles * num_kv_heads;
+  if (base >= 1024) return 1;
+  const long want = (2048 + base - 1) / base;
+  const long cap = std::max(1, max_kv_len / 256);
+  return (int)std::max(1L, std::min(want, cap));
+}
+
+int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, int* chunk) {
+  int s = requested;
+  if (s <= 0) {
+    const long pairs = (long)batch * num_kv_heads;
+    const long want = std::max(1L, (2048 + pairs - 1) / pairs);
+    const long cap = std::max(1, (max_kv_len + kDecodeChunkMin - 1) / kDecodeChunkMin);
+    s = (int)std::min(want, cap);
+  }
+  // slice length: a multiple of 4 waves x 32 tokens covering max_kv_len in s slices
+  int c = (max_kv_len + s - 1) / s;
+  c = ((c + 127) / 128) * 128;
+  if (c < 128) c = 128;
+  *chunk = c;
+  return s;
+}
+
+bool group_ok(int g) { return g >= 1 && g <= 64 && (256 % g) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4kv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t nvfp4kv_version(void) { return 100; }
+
+int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
+                    int64_t k_token_stride, int64_t v_token_stride, const int64_t* slot_mapping,
+                    int32_t num_tokens, void* stream) {
+  if (int e = check_cache(cache)) return e;
+  if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(NVFP4KV_EINVAL, "k, v or slot_mapping is NULL");
+  const int64_t row = (int64_t)cache->num_kv_heads * cache->head_dim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(NVFP4KV_EINVAL, "token stride smaller than num_kv_heads * head_dim");
+  if ((k_token_stride % 8) || (v_token_stride % 8) || !aligned16(k) || !aligned16(v))
+    return fail(NVFP4KV_EINVAL, "k/v must be 16-byte aligned with token strides a multiple of 8");
+  nvfp4kv::AppendParams p{};
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.k_stride = k_token_stride;
+  p.v_stride = v_token_stride;
+  p.slots = slot_mapping;
+  p.k_data = cache->k_data;
+  p.k_scale = cache->k_scale;
+  p.v_data = cache->v_data;
+  p.v_scale = cache->v_scale;
+  p.k_global = cache->k_global;
+  p.v_global = cache->v_global;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  return check_launch(nvfp4kv::launch_append(p, (hipStream_t)stream), "append launch");
+}
+
+size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_kv_len, int32_t num_qo_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t num_splits) {
+  if (batch <= 0 || total_q <= 0 || max_q_len <= 0 || num_kv_heads <= 0 || num_qo_heads <= 0 ||
+      head_dim != 128 || num_qo_heads % num_kv_heads)
+    return 0;
+  const int g = num_qo_heads / num_kv_heads;
+  if (!group_ok(g)) return 0;
+  const int nw = prefill_waves(max_q_len, g);
+  const int q_tiles = (max_q_len + (32 * nw / g) - 1) / (32 * nw / g);
+  const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, num_splits);
+  if (s <= 1) return 0;
+  return (size_t)s * total_q * num_qo_heads * (head_dim + 1) * sizeof(float);
+}
+
+int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_seqlens_q,
+                        const int32_t* kv_lens, const int32_t* block_table,
+                        int32_t block_table_stride, int32_t batch, int32_t total_q,
+                        int32_t max_q_len, int32_t max_kv_len, int32_t num_qo_heads,
+                        float sm_scale, int32_t causal, void* out, int32_t out_dtype, float* lse,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (int e = check_cache(cache)) return e;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0)
+    return fail(NVFP4KV_EINVAL, "negative size");
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!q || !cu_seqlens_q || !kv_lens || !block_table || !out)
+    return fail(NVFP4KV_EINVAL, "q, cu_seqlens_q, kv_lens, block_table or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4KV_EINVAL, "q/out must be 16-byte aligned");
+  if (num_qo_heads < 1 || num_qo_heads % cache->num_kv_heads)
+    return fail(NVFP4KV_EINVAL, "num_qo_heads %d is not a multiple of num_kv_heads %d", num_qo_heads,
+                cache->num_kv_heads);
+  const int g = num_qo_heads / cache->num_kv_heads;
+  if (!group_ok(g)) return fail(NVFP4KV_EUNSUPPORTED, "query group size %d unsupported", g);
+  if (block_table_stride < (max_kv_len + 15) / 16)
+    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
+                block_table_stride, max_kv_len);
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "sm_scale must be > 0");
+  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32)
+    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
+  if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
+
+  const int nw = prefill_waves(max_q_len, g);
+  const int rows = 32 * nw / g;
+  const int q_tiles = (max_q_len + rows - 1) / rows;
+  const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, num_splits);
+  const long items = (long)cache->num_kv_heads * batch * q_tiles * s;
+  if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
+
+  nvfp4kv::PrefillParams p{};
+  p.k_data = cache->k_data;
+  p.k_scale = cache->k_scale;
+  p.v_data = cache->v_data;
+  p.v_scale = cache->v_scale;
+  p.q = (const uint16_t*)q;
+  p.cu_q = cu_seqlens_q;
+  p.kv_lens = kv_lens;
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.batch = batch;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_qo_heads = num_qo_heads;
+  p.group = g;
+  p.q_tiles = q_tiles;
+  p.num_splits = s;
+  p.causal = causal ? 1 : 0;
+  p.total_q = total_q;
+  p.total_items = (int)items;
+  p.items_per_xcd = (int)((items + 7) / 8);
+  p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
+  p.out_scale = cache->v_global;
+  p.out_f32 = out_dtype == NVFP4KV_OUT_F32;
+  hipStream_t st = (hipStream_t)stream;
+  if (s > 1) {
+    const size_t need = (size_t)s * total_q * num_qo_heads * (128 + 1) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+      return fail(NVFP4KV_EWORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
+    p.part_o = (float*)workspace;
+    p.part_lse = p.part_o + (size_t)s * total_q * num_qo_heads * 128;
+    p.lse = nullptr;
+    p.out = nullptr;
+    if (int e = check_launch(nvfp4kv::launch_prefill(p, nw, st), "prefill launch")) return e;
+    nvfp4kv::MergeParams m{};
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.num_splits = s;
+    m.rows = total_q * num_qo_heads;
+    m.out_scale = cache->v_global;
+    m.out = out;
+    m.out_f32 = p.out_f32;
+    m.lse = lse;
+    return check_launch(nvfp4kv::launch_merge(m, st), "merge launch");
+  }
+  p.lse = lse;
+  p.out = out;
+  return check_launch(nvfp4kv::launch_prefill(p, nw, st), "prefill launch");
+}
+
+size_t paged_decode_nvfp4_workspace_size(int32_t batch, int32_t max_kv_len, int32_t num_qo_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t num_splits) {
+  if (batch <= 0 || max_kv_len <= 0 || num_kv_heads <= 0 || num_qo_heads <= 0 || head_dim != 128)
+    return 0;
+  int chunk = 0;
+  const int s = decode_splits(batch, num_kv_heads, max_kv_len, num_splits, &chunk);
+  return (size_t)s * batch * num_qo_heads * (head_dim + 1) * sizeof(float);
+}
+
+int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* kv_lens,
+                       const int32_t* block_table, int32_t block_table_stride, int32_t batch,
+                       int32_t max_kv_len, int32_t num_qo_heads, float sm_scale, void* out,
+                       int32_t out_dtype, float* lse, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (int e = check_cache(cache)) return e;
+  if (batch < 0 || max_kv_len < 0) return fail(NVFP4KV_EINVAL, "negative size");
+  if (batch == 0) return ok();
+  if (!q || !kv_lens || !block_table || !out)
+    return fail(NVFP4KV_EINVAL, "q, kv_lens, block_table or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4KV_EINVAL, "q/out must be 16-byte aligned");
+  if (num_qo_heads < 1 || num_qo_heads % cache->num_kv_heads)
+    return fail(NVFP4KV_EINVAL, "num_qo_heads %d is not a multiple of num_kv_heads %d", num_qo_heads,
+                cache->num_kv_heads);
+  const int g = num_qo_heads / cache->num_kv_heads;
+  if (g > 16) return fail(NVFP4KV_EUNSUPPORTED, "decode supports query groups of at most 16 (got %d)", g);
+  if (max_kv_len < 1) return fail(NVFP4KV_EINVAL, "max_kv_len must be >= 1");
+  if (block_table_stride < (max_kv_len + 15) / 16)
+    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
+                block_table_stride, max_kv_len);
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "sm_scale must be > 0");
+  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32)
+    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
+  if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
+  int chunk = 0;
+  const int s = decode_splits(batch, cache->num_kv_heads, max_kv_len, num_splits, &chunk);
+  const long items = (long)cache->num_kv_heads * batch * s;
+  if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
+  const size_t need = (size_t)s * batch * num_qo_heads * (128 + 1) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4KV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
+
+  nvfp4kv::DecodeParams p{};
+  p.k_data = cache->k_data;
+  p.k_scale = cache->k_scale;
+  p.v_data = cache->v_data;
+  p.v_scale = cache->v_scale;
+  p.q = (const uint16_t*)q;
+  p.kv_lens = kv_lens;
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.batch = batch;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_qo_heads = num_qo_heads;
+  p.group = g;
+  p.num_splits = s;
+  p.chunk = chunk;
+  p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
+  p.part_o = (float*)workspace;
+  p.part_lse = p.part_o + (size_t)s * batch * num_qo_heads * 128;
+  hipStream_t st = (hipStream_t)stream;
+  if (int e = check_launch(nvfp4kv::launch_decode(p, st), "decode launch")) return e;
+  nvfp4kv::MergeParams m{};
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.num_splits = s;
+  m.rows = batch * num_qo_heads;
+  m.out_scale = cache->v_global;
+  m.out = out;
+  m.out_f32 = out_dtype == NVFP4KV_OUT_F32;
+  m.lse = lse;
+  return check_launch(nvfp4kv::launch_merge(m, st), "merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+// Split-KV single-token paged decode over the NVFP4 KV cache for gfx950.
+//
+// Decode reads the whole growing cache for one query token per sequence and is bound by HBM
+// bandwidth ("NVFP4 KV cache prefill vs decode performance", sections "NVFP4 KV cache prefill vs
+// decode performance" and "Decode can win on fewer bytes read").  The kernel therefore spends as
+// little as possible per cache byte:
+//
+//  * A workgroup (4 wavefronts) owns one (sequence, KV head, key slice).  Each wavefront walks a
+//    contiguous quarter of the slice in steps of 32 tokens; all query heads of the group ride
+//    along as MFMA columns, so each packed byte is read and converted exactly once.
+//  * K goes from HBM straight into MFMA operand registers: lane l loads 16 bytes of one token
+//    (32 head-dim values) and converts them, scaled, to bf16.  The head-dim order inside each
+//    32-wide k-step is permuted identically for K and Q, which leaves the dot products unchanged
+//    and lets every lane use one 16-byte load.  Scores: S^T = K Q^T with 16x16x32 bf16 MFMA.
+//  * V is converted the same way into a small per-wavefront LDS stage and read back with the
+//    transposing LDS load as the A operand of O^T = V^T P^T; P^T needs no data movement.
+//  * Online softmax in base 2 with lazy rescaling (refresh when the maximum grows by > 8).
+//  * The four wavefronts are combined in LDS; one partial (o, log2-sum-exp) per (sequence, query
+//    head, slice) goes to the workspace, and a merge kernel reduces the slices.
+//  * The workgroup -> (KV head, sequence, slice) map keeps each KV head on one XCD.
+#include "device_common.hpp"
+#include "kernel_params.hpp"
+
+namespace nvfp4kv {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecStep = 32;
+constexpr int kDecVStride = 288;  // bytes per staged V row (256 + 32 pad for transposed reads)
+constexpr int kDecStageBytes = kDecStep * kDecVStride;
+
+struct DecodeRegs {
+  u32x4 kd[2], vd[2];
+  uint32_t ks[2], vs[2];
+};
+
+__device__ __forceinline__ void decode_load(const DecodeParams& p, const int32_t* bt_row, int hk,
+                                            int kv_len, int k, int lane, DecodeRegs& r) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int first = k + 16 * g;  // wave-uniform; 16-aligned, so one page per group
+    const int tok = first + (lane & 15);
+    r.kd[g] = r.vd[g] = u32x4{0u, 0u, 0u, 0u};
+    r.ks[g] = r.vs[g] = 0u;
+    if (first < kv_len) {
+      const int page = bt_row[uniform(first >> 4)];
+      if (tok < kv_len) {
+        const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (tok & 15);
+        const int q4 = lane >> 4;
+        r.kd[g] = *(const u32x4*)(p.k_data + row * kRowBytes + 16 * q4);
+        r.vd[g] = *(const u32x4*)(p.v_data + row * kRowBytes + 16 * q4);
+        r.ks[g] = *(const uint16_t*)(p.k_scale + row * kScaleBytes + 2 * q4);
+        r.vs[g] = *(const uint16_t*)(p.v_scale + row * kScaleBytes + 2 * q4);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kDecWaves * kDecStageBytes];
+  __shared__ float red_m[kDecWaves][16];
+  __shared__ float red_l[kDecWaves][16];
+
+  const int wg = blockIdx.x;
+  const int ipx = (p.num_kv_heads * p.batch * p.num_splits + 7) / 8;
+  const int item = (wg & 7) * ipx + (wg >> 3);
+  if (item >= p.num_kv_heads * p.batch * p.num_splits) return;
+  const int split = item % p.num_splits;
+  const int b = (item / p.num_splits) % p.batch;
+  const int hk = item / (p.num_splits * p.batch);
+
+  const int G = p.group;
+  const int Hq = p.num_qo_heads;
+  const int kv_len = p.kv_lens[b];
+  const int key_begin = split * p.chunk;
+  const int64_t prow0 = ((int64_t)split * p.batch + b) * Hq + hk * G;  // first partial row
+  if (key_begin >= kv_len) {
+    if (threadIdx.x < G) p.part_lse[prow0 + threadIdx.x] = kNegInf;
+    return;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  const bool colv = col < G;
+
+  bf16x8 qf[4];
+  {
+    const uint16_t* qp = p.q + ((int64_t)b * Hq + hk * G + (colv ? col : 0)) * kHeadDim + 32 * q4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 v = colv ? *(const u32x4*)(qp + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const int per_wave = p.chunk / kDecWaves;
+  const int wk0 = key_begin + w * per_wave;
+  const int wk1 = min(kv_len, wk0 + per_wave);
+  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+  const float cs = p.score_scale;
+  char* stage = smem + w * kDecStageBytes;
+
+  f32x4 acc_o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc_o[i] = f32x4{};
+  float m_used = kNegInf;
+  float l_part = 0.0f;
+
+  DecodeRegs cur;
+  if (wk0 < wk1) decode_load(p, bt_row, hk, kv_len, wk0, lane, cur);
+  for (int k = wk0; k < wk1; k += kDecStep) {
+    DecodeRegs nxt;
+    const bool more = k + kDecStep < wk1;
+    if (more) decode_load(p, bt_row, hk, kv_len, k + kDecStep, lane, nxt);
+
+    // ---- scores for 2 x 16 tokens
+    f32x4 sc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float s0 = e4m3_byte<0>(cur.ks[g]);
+      const float s1 = e4m3_byte<1>(cur.ks[g]);
+      f32x4 a = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t o4[4];
+        dequant8(cur.kd[g][kk], kk < 2 ? s0 : s1, o4);
+        a = mfma16(__builtin_bit_cast(bf16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
+      }
+      sc[g] = a;
+    }
+    // ---- stage V (bf16, row-major [token][d]) for the transposed operand reads
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float s0 = e4m3_byte<0>(cur.vs[g]);
+      const float s1 = e4m3_byte<1>(cur.vs[g]);
+      uint32_t o[16];
+      dequant8(cur.vd[g][0], s0, o + 0);
+      dequant8(cur.vd[g][1], s0, o + 4);
+      dequant8(cur.vd[g][2], s1, o + 8);
+      dequant8(cur.vd[g][3], s1, o + 12);
+      char* dst = stage + (16 * g + (lane & 15)) * kDecVStride + 64 * q4;
+      *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
+      *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
+      *(u32x4*)(dst + 32) = u32x4{o[8], o[9], o[10], o[11]};
+      *(u32x4*)(dst + 48) = u32x4{o[12], o[13], o[14], o[15]};
+    }
+    // ---- mask tokens past the wave's range, then online softmax
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (k + 16 * g + 4 * q4 + j >= wk1) sc[g][j] = kNegInf;
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[0][j], sc[1][j]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = pair32_max(mx) * cs;
+    if (wave_any(mx > m_used + 8.0f)) {
+      const float m_new = fmaxf(m_used, mx);
+      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc_o[i] *= alpha;
+      l_part *= alpha;
+      m_used = m_new;
+    }
+    const float mref = (m_used == kNegInf) ? 0.0f : m_used;
+    bf16x8 pb;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = fast_exp2(fmaf(sc[g][j], cs, -mref));
+        l_part += e;
+        pb[4 * g + j] = (__bf16)e;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- O^T += V^T P^T over 8 blocks of 16 head-dim values
+    const int t16 = lane & 15;
+    const char* lo_row = stage + (4 * q4 + (t16 >> 2)) * kDecVStride + 8 * (t16 & 3);
+    const char* hi_row = lo_row + 16 * kDecVStride;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const i16x4 lo = lds_read_tr16(lo_row + 32 * mb);
+      const i16x4 hi = lds_read_tr16(hi_row + 32 * mb);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_o[mb] = mfma16(a, pb, acc_o[mb]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (more) cur = nxt;
+  }
+
+  // ---- combine the four wavefronts in LDS
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  l_tot = pair32_sum(l_tot);
+  __syncthreads();  // every wavefront is done with its V stage
+  float* red_o = (float*)smem;  // [wave][16 columns][128]
+  if (q4 == 0) {
+    red_m[w][col] = m_used;
+    red_l[w][col] = l_tot;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+    *(f32x4*)(red_o + (w * 16 + col) * kHeadDim + 16 * mb + 4 * q4) = acc_o[mb];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
+    const int c = idx >> 7;
+    const int d = idx & 127;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, red_m[ww][c]);
+    float L = 0.0f, o = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < kDecWaves; ++ww) {
+        const float mw = red_m[ww][c];
+        const float wt = mw == kNegInf ? 0.0f : fast_exp2(mw - M);
+        L = fmaf(wt, red_l[ww][c], L);
+        o = fmaf(wt, red_o[(ww * 16 + c) * kHeadDim + d], o);
+      }
+    }
+    p.part_o[(prow0 + c) * kHeadDim + d] = L > 0.0f ? o / L : 0.0f;
+    if (d == 0) p.part_lse[prow0 + c] = L > 0.0f ? M + __log2f(L) : kNegInf;
+  }
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  const int items = p.num_kv_heads * p.batch * p.num_splits;
+  const dim3 grid((unsigned)(8 * ((items + 7) / 8)));
+  hipLaunchKernelGGL(nvfp4_decode_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

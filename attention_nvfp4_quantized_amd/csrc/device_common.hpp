@@ -1,0 +1,96 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types, MFMA wrappers,
+// the NVFP4 read-side conversion and a few cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kHeadDim = 128;
+constexpr int kPageSize = 16;
+constexpr int kRowBytes = kHeadDim / 2;      // packed bytes per (token, head)
+constexpr int kScaleBytes = kHeadDim / 16;   // scale bytes per (token, head)
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// D(32x32) += A(32x16) * B(16x32).  Lane l holds A[l%32][8(l/32)+i], B[8(l/32)+i][l%32],
+// D[8(j/4)+4(l/32)+j%4][l%32] (j = 0..15).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// D(16x16) += A(16x32) * B(32x16).  Lane l holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16],
+// D[4(l/16)+j][l%16] (j = 0..3).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// E4M3FN scale byte SEL of `word` -> float (exact: the hardware conversion agrees with the
+// format definition on all 256 codes).
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8(word, SEL);
+}
+
+// Two E2M1 codes (byte SEL of `word`) -> their values as floats, unscaled and exact.
+// The conversion's own scale operand only applies a power of two, so block scales are applied
+// by a separate exact multiply.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1_pair(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight E2M1 codes in `word` (element 0 in the low nibble) times scale s -> four bf16x2 words.
+// Every product has at most 6 significant bits, so the bf16 results are exact.
+__device__ __forceinline__ void dequant8(uint32_t word, float s, uint32_t out[4]) {
+  f32x2 a = e2m1_pair<0>(word);
+  f32x2 b = e2m1_pair<1>(word);
+  f32x2 c = e2m1_pair<2>(word);
+  f32x2 d = e2m1_pair<3>(word);
+  out[0] = pack_bf16x2(a[0] * s, a[1] * s);
+  out[1] = pack_bf16x2(b[0] * s, b[1] * s);
+  out[2] = pack_bf16x2(c[0] * s, c[1] * s);
+  out[3] = pack_bf16x2(d[0] * s, d[1] * s);
+}
+
+// Reductions over the lane pair (l, l^32).  (permlane32_swap with the same value in both
+// operands is miscompiled -- both results come back as the partner's value -- so the exchange
+// goes through ds_bpermute.)
+__device__ __forceinline__ float pair32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float pair32_sum(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Block of LDS data read with the gfx950 transposing load: within each group of 16 lanes, the
+// lane at position t receives element t%4 of the 4-element rows supplied by lanes t/4 + 4k
+// (k = 0..3).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+}
+
+__device__ __forceinline__ int wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+}  // namespace nvfp4kv

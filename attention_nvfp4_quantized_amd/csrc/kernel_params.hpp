@@ -1,0 +1,90 @@
+// Argument blocks passed from the C-ABI layer to the kernel launchers (host and device visible).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+struct AppendParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_stride;  // elements between tokens
+  int64_t v_stride;
+  const int64_t* slots;
+  uint8_t* k_data;
+  uint8_t* k_scale;
+  uint8_t* v_data;
+  uint8_t* v_scale;
+  float k_global;
+  float v_global;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+};
+
+struct PrefillParams {
+  const uint8_t* k_data;
+  const uint8_t* k_scale;
+  const uint8_t* v_data;
+  const uint8_t* v_scale;
+  const uint16_t* q;
+  const int32_t* cu_q;
+  const int32_t* kv_lens;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t num_qo_heads;
+  int32_t group;
+  int32_t q_tiles;        // ceil(max_q_len / rows_per_tile)
+  int32_t num_splits;
+  int32_t causal;
+  int32_t total_q;
+  int32_t items_per_xcd;  // ceil(total_items / 8)
+  int32_t total_items;    // num_kv_heads * batch * q_tiles * num_splits
+  float score_scale;      // sm_scale * k_global * log2(e)
+  float out_scale;        // v_global
+  float* lse;             // optional [total_q][Hq] (natural log); unused in split mode
+  void* out;              // [total_q][Hq][D]
+  int32_t out_f32;
+  float* part_o;          // split mode: [num_splits][total_q][Hq][D]
+  float* part_lse;        // split mode: [num_splits][total_q][Hq] (log2 units)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  int32_t num_splits;
+  int32_t rows;          // total_q * Hq
+  float out_scale;
+  void* out;
+  int32_t out_f32;
+  float* lse;
+};
+
+struct DecodeParams {
+  const uint8_t* k_data;
+  const uint8_t* k_scale;
+  const uint8_t* v_data;
+  const uint8_t* v_scale;
+  const uint16_t* q;
+  const int32_t* kv_lens;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t num_qo_heads;
+  int32_t group;
+  int32_t num_splits;
+  int32_t chunk;          // keys per split (multiple of 64)
+  float score_scale;
+  float* part_o;          // [num_splits][batch][Hq][D]
+  float* part_lse;        // [num_splits][batch][Hq]
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace nvfp4kv

@@ -1,0 +1,332 @@
+// Causal paged prefill over the NVFP4 KV cache for gfx950 (CDNA4).
+//
+// What is computed is the stock read path of "NVFP4 KV cache A4Q prefill explained" (section
+// "Why NVFP4 KV cache A4Q prefill exists"): the packed K and V are unpacked, converted and
+// scaled, and attention runs with bf16 queries.  The design is MI355X-first:
+//
+//  * A workgroup owns one KV head, one tile of query positions and (optionally) one slice of
+//    the key range.  Its query "columns" are (position, head-of-group) pairs, so all query heads
+//    that share the KV head use every dequantized KV tile: the unpack/scale work is paid once
+//    per 64-key tile and amortised over 32 * waves columns.
+//  * Each 64-key tile is loaded packed from HBM (72 B per key and head for each of K and V),
+//    dequantized exactly to bf16 and written to LDS; the next tile's loads are in flight while
+//    the current tile is consumed (two LDS buffers, one barrier per tile).
+//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA: each lane then holds
+//    16 keys of one query column per 32-key block, so the softmax row reduction is lane-local
+//    plus one permlane32 swap, and P^T is already the B operand of O^T = V^T P^T.  V^T operands
+//    come straight from the row-major V tile through the transposing LDS read.
+//  * Online softmax in base 2 with the running maximum refreshed only when a tile's maximum
+//    exceeds it by more than 8 (factor 256), which keeps P <= 256 and skips most rescales.
+//  * Causal tile skipping: a workgroup walks only the keys its last row can see; waves whose
+//    rows cannot see a tile skip its MFMAs; masks are applied only on tiles that need them.
+//  * The workgroup -> work-item map sends all work of one KV head to one XCD (its L2 holds that
+//    head's packed cache) and orders query tiles longest first.
+#include "device_common.hpp"
+#include "kernel_params.hpp"
+
+namespace nvfp4kv {
+
+constexpr int kTileKeys = 64;
+constexpr int kKStride = 272;  // LDS bytes per K row: 256 + 16 pad (conflict-free b128 reads)
+constexpr int kVStride = 288;  // LDS bytes per V row: 256 + 32 pad (conflict-free transposed reads)
+constexpr int kKTileBytes = kTileKeys * kKStride;
+constexpr int kVTileBytes = kTileKeys * kVStride;
+constexpr int kBufBytes = kKTileBytes + kVTileBytes;
+
+template <int NW>
+struct TileRegs {
+  static constexpr int kItems = 512 / (64 * NW);  // 16-byte chunks per thread per tile
+  u32x4 data[kItems];
+  uint32_t scale[kItems];
+};
+
+// Load the packed K and V chunks of tile `kt` that this thread dequantizes.  Chunk `it` of the
+// tile: X = it / 256 (K or V), key = (it % 256) / 4, quarter = it % 4 (32 head-dim values).
+// A wavefront's 64 chunks are the 16 keys of one page, so the page id is wave-uniform.
+template <int NW>
+__device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t* bt_row, int hk,
+                                          int kv_len, int kt, TileRegs<NW>& r) {
+#pragma unroll
+  for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
+    const int it = threadIdx.x + 64 * NW * j;
+    const int X = it >> 8;
+    const int key = (it & 255) >> 2;
+    const int qq = it & 3;
+    const int gkey = kt * kTileKeys + key;
+    const int first_key = uniform(kt * kTileKeys + (((it & 255) >> 2) & ~15));
+    r.data[j] = u32x4{0u, 0u, 0u, 0u};
+    r.scale[j] = 0u;
+    if (first_key < kv_len) {
+      const int page = bt_row[uniform(first_key >> 4)];
+      if (gkey < kv_len) {
+        const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (gkey & 15);
+        const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
+        const uint8_t* sp = (X == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq;
+        r.data[j] = *(const u32x4*)dp;
+        r.scale[j] = *(const uint16_t*)sp;
+      }
+    }
+  }
+}
+
+// Dequantize the loaded chunks to bf16 and write them to an LDS tile buffer.
+template <int NW>
+__device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW>& r) {
+#pragma unroll
+  for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
+    const int it = threadIdx.x + 64 * NW * j;
+    const int X = it >> 8;
+    const int key = (it & 255) >> 2;
+    const int qq = it & 3;
+    const float s0 = e4m3_byte<0>(r.scale[j]);
+    const float s1 = e4m3_byte<1>(r.scale[j]);
+    uint32_t o[16];
+    dequant8(r.data[j][0], s0, o + 0);
+    dequant8(r.data[j][1], s0, o + 4);
+    dequant8(r.data[j][2], s1, o + 8);
+    dequant8(r.data[j][3], s1, o + 12);
+    char* dst = buf + (X == 0 ? key * kKStride : kKTileBytes + key * kVStride) + 64 * qq;
+    *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
+    *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
+    *(u32x4*)(dst + 32) = u32x4{o[8], o[9], o[10], o[11]};
+    *(u32x4*)(dst + 48) = u32x4{o[12], o[13], o[14], o[15]};
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+
+  // ---- work item: XCD-major so one KV head's items share an XCD; query tiles longest first.
+  const int wg = blockIdx.x;
+  const int item = (wg & 7) * p.items_per_xcd + (wg >> 3);
+  if (item >= p.total_items) return;
+  const int split = item % p.num_splits;
+  int r = item / p.num_splits;
+  const int qt = p.q_tiles - 1 - (r % p.q_tiles);
+  r /= p.q_tiles;
+  const int b = r % p.batch;
+  const int hk = r / p.batch;
+
+  constexpr int kCols = 32 * NW;
+  const int G = p.group;
+  const int rows_per_tile = kCols / G;
+  const int q_start = p.cu_q[b];
+  const int q_len = p.cu_q[b + 1] - q_start;
+  const int pos0 = qt * rows_per_tile;
+  if (pos0 >= q_len) return;
+  const int kv_len = p.kv_lens[b];
+  const int pos_last = min(q_len, pos0 + rows_per_tile) - 1;
+  const int shift = p.causal ? kv_len - q_len : 0;  // row i sees keys <= i + shift
+  const int lim_tile = p.causal ? shift + pos_last : kv_len - 1;
+  const int n_keys = max(0, min(kv_len, lim_tile + 1));
+  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
+  const int per_split = (n_tiles + p.num_splits - 1) / p.num_splits;
+  const int t_begin = split * per_split;
+  const int t_end = min(n_tiles, t_begin + per_split);
+
+  // ---- this lane's query column
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int h32 = lane >> 5;
+  const int col = 32 * w + (lane & 31);
+  const int pos = pos0 + col / G;
+  const int head = hk * G + col % G;
+  const bool valid = pos <= pos_last;
+  const int lim = valid ? (p.causal ? shift + pos : kv_len - 1) : -1;
+  // wave-uniform bounds of the keys this wave's rows can see
+  const int wpos_first = pos0 + (32 * w) / G;
+  const int wpos_last = pos0 + (32 * w + 31) / G;
+  const bool wave_active = wpos_first <= pos_last;
+  const int wlim_max = !wave_active ? -1 : (p.causal ? shift + min(wpos_last, pos_last) : kv_len - 1);
+  const int wlim_min = (!wave_active || wpos_last > pos_last) ? -1 : (p.causal ? shift + wpos_first : kv_len - 1);
+
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = p.q + ((int64_t)(q_start + (valid ? pos : 0)) * p.num_qo_heads + head) * kHeadDim + 8 * h32;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      u32x4 v = valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+      qf[t] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
+  float m_used = kNegInf;
+  float l_part = 0.0f;
+  const float cs = p.score_scale;
+
+  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+  const int g16 = lane >> 4;  // 16-lane group
+  const int t16 = lane & 15;
+
+  if (t_begin < t_end) {
+    TileRegs<NW> regs;
+    load_tile<NW>(p, bt_row, hk, kv_len, t_begin, regs);
+    store_tile<NW>(smem, regs);
+    __syncthreads();
+
+    for (int kt = t_begin; kt < t_end; ++kt) {
+      char* buf = smem + ((kt - t_begin) & 1) * kBufBytes;
+      const bool more = kt + 1 < t_end;
+      if (more) load_tile<NW>(p, bt_row, hk, kv_len, kt + 1, regs);
+
+      const int k0 = kt * kTileKeys;
+      if (k0 <= wlim_max) {
+        // ---- S^T = K Q^T for 64 keys x 32 columns
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        const char* kb = buf + (lane & 31) * kKStride + 16 * h32;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 a0 = *(const bf16x8*)(kb + 32 * t);
+          const bf16x8 a1 = *(const bf16x8*)(kb + 32 * kKStride + 32 * t);
+          s0 = mfma32(a0, qf[t], s0);
+          s1 = mfma32(a1, qf[t], s1);
+        }
+        if (k0 + kTileKeys - 1 > wlim_min) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + 8 * (j >> 2) + 4 * h32 + (j & 3);
+            if (key > lim) s0[j] = kNegInf;
+            if (key + 32 > lim) s1[j] = kNegInf;
+          }
+        }
+        // ---- online softmax (base 2)
+        float mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+        mx = pair32_max(mx) * cs;
+        if (wave_any(mx > m_used + 8.0f)) {
+          const float m_new = fmaxf(m_used, mx);
+          const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
+          l_part *= alpha;
+          m_used = m_new;
+        }
+        const float mref = (m_used == kNegInf) ? 0.0f : m_used;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e0 = fast_exp2(fmaf(s0[j], cs, -mref));
+          const float e1 = fast_exp2(fmaf(s1[j], cs, -mref));
+          l_part += e0 + e1;
+          pb[(j >> 3)][j & 7] = (__bf16)e0;
+          pb[2 + (j >> 3)][j & 7] = (__bf16)e1;
+        }
+        // ---- O^T += V^T P^T: 4 d-blocks x (2 key blocks x 2 k-steps)
+        const char* vb = buf + kKTileBytes;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int key0 = 16 * u + 4 * h32 + (t16 >> 2);  // u = 2 * mb + ks
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int d0 = 32 * db + 16 * (g16 & 1) + 4 * (t16 & 3);
+            const i16x4 lo = lds_read_tr16(vb + key0 * kVStride + 2 * d0);
+            const i16x4 hi = lds_read_tr16(vb + (key0 + 8) * kVStride + 2 * d0);
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc_o[db] = mfma32(a, pb[u], acc_o[db]);
+          }
+        }
+      }
+      if (more) store_tile<NW>(smem + (((kt + 1 - t_begin) & 1) * kBufBytes), regs);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue
+  const float l_tot = pair32_sum(l_part);
+  if (!valid) return;
+  const int64_t orow = (int64_t)(q_start + pos) * p.num_qo_heads + head;
+  if (p.num_splits > 1) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float* po = p.part_o + ((int64_t)split * p.total_q * p.num_qo_heads + orow) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * h32;
+        *(f32x4*)(po + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
+                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
+      }
+    if (h32 == 0)
+      p.part_lse[(int64_t)split * p.total_q * p.num_qo_heads + orow] =
+          l_tot > 0.0f ? m_used + __log2f(l_tot) : kNegInf;
+    return;
+  }
+  const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
+  if (p.out_f32) {
+    float* op = (float*)p.out + orow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * h32;
+        *(f32x4*)(op + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
+                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
+      }
+  } else {
+    uint16_t* op = (uint16_t*)p.out + orow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * h32;
+        *(u32x2*)(op + d) = u32x2{pack_bf16x2(acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv),
+                                  pack_bf16x2(acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv)};
+      }
+  }
+  if (p.lse && h32 == 0) p.lse[orow] = l_tot > 0.0f ? (m_used + __log2f(l_tot)) * kLn2 : kNegInf;
+}
+
+// Log-sum-exp merge of split partials: one wavefront per (query row, head); lane l owns
+// head-dim values 2l and 2l+1.
+__global__ __launch_bounds__(256) void nvfp4_merge_kernel(MergeParams p) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  const int lane = threadIdx.x & 63;
+  float mx = kNegInf;
+  for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, p.part_lse[(int64_t)s * p.rows + row]);
+  float wsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < p.num_splits; ++s) {
+      const float ls = p.part_lse[(int64_t)s * p.rows + row];
+      if (ls == kNegInf) continue;  // empty slice: its partial o is not written
+      const float wgt = fast_exp2(ls - mx);
+      const f32x2 v = *(const f32x2*)(p.part_o + ((int64_t)s * p.rows + row) * kHeadDim + 2 * lane);
+      wsum += wgt;
+      o0 = fmaf(wgt, v[0], o0);
+      o1 = fmaf(wgt, v[1], o1);
+    }
+  }
+  const float inv = wsum > 0.0f ? p.out_scale / wsum : 0.0f;
+  if (p.out_f32) {
+    *(f32x2*)((float*)p.out + (int64_t)row * kHeadDim + 2 * lane) = f32x2{o0 * inv, o1 * inv};
+  } else {
+    *(uint32_t*)((uint16_t*)p.out + (int64_t)row * kHeadDim + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+  }
+  if (p.lse && lane == 0) p.lse[row] = wsum > 0.0f ? (mx + __log2f(wsum)) * kLn2 : kNegInf;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream) {
+  const dim3 grid((unsigned)(8 * p.items_per_xcd));
+  switch (waves) {
+    case 8: hipLaunchKernelGGL(nvfp4_prefill_kernel<8>, grid, dim3(512), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(nvfp4_prefill_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(nvfp4_prefill_kernel<2>, grid, dim3(128), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(nvfp4_prefill_kernel<1>, grid, dim3(64), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.rows + 3) / 4));
+  hipLaunchKernelGGL(nvfp4_merge_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

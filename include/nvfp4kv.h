@@ -1,0 +1,148 @@
+/*
+ * nvfp4kv.h -- C ABI of the NVFP4 paged KV-cache attention library for AMD MI355X (gfx950).
+ *
+ * The operations follow the three "fanout.sh" pages on NVFP4 KV caches:
+ *   [A] "NVFP4 KV cache A4Q prefill explained"
+ *   [B] "NVFP4 KV cache prefill vs decode performance"
+ *   [C] "NVFP4 KV cache vs NVFP4 weights"
+ *
+ * Cache format ([B] "NVFP4 stores 4.5 bits per value before padding"; [C] "NVFP4 KV cache vs
+ * NVFP4 weights"): every value is a 4-bit E2M1 code, two codes per byte, and every block of 16
+ * consecutive head-dim values of one (token, KV head) carries one E4M3 (OCP "FN") scale byte:
+ * 72 bits per 16 values.  A per-tensor scale g (k_global / v_global) maps values into the block
+ * range: the writer quantizes x / g and the reader multiplies by g.
+ *
+ * Element code: sign bit 3 copied from the input, magnitude = round-to-nearest-even of |x/g| / s
+ * on the grid {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6.  Block scale: s = E4M3 round-to-
+ * nearest-even of fl32(amax / 6), saturating at 448; a zero scale gives magnitude 0.  Byte i of a
+ * row holds element 2i in its low nibble and element 2i+1 in its high nibble.
+ *
+ * Page layout (per layer; X in {K, V}; page_size 16, head_dim 128):
+ *   X_data  : uint8 [num_pages][num_kv_heads][16][head_dim / 2]
+ *   X_scale : uint8 [num_pages][num_kv_heads][16][head_dim / 16]     (linear, not swizzled)
+ * A cache slot is page * 16 + offset.  Pages are reached through a block table
+ * (int32 [batch][block_table_stride]: page ids of positions 0, 16, 32, ...).
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers except `cache` itself are device pointers owned by the caller; `cache` is a
+ *     host pointer to a descriptor holding device pointers.  `stream` is a hipStream_t (NULL =
+ *     the default stream).  Calls are asynchronous on `stream`.
+ *   - The library never allocates, frees or synchronizes.  Entry points that need scratch memory
+ *     take a caller-provided workspace and report its size through a *_workspace_size call.
+ *   - Only the cache (append), `out`, `lse` and `workspace` are written.
+ *   - Return value: 0 on success, otherwise a negative NVFP4KV_E* code; the message of the last
+ *     failure on the calling thread is returned by nvfp4kv_last_error().  Unsupported shapes are
+ *     rejected; there is no fallback path.
+ *   - Device-side index contents are the caller's contract (checked only where the host knows
+ *     them): slots and block-table entries must address allocated pages, kv_len >= q_len for
+ *     causal prefill, slots within one append call must be distinct.
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4KV_OK 0
+#define NVFP4KV_EINVAL (-1)       /* null pointer, bad size or inconsistent arguments */
+#define NVFP4KV_EUNSUPPORTED (-2) /* head_dim != 128, page_size != 16, unsupported group size */
+#define NVFP4KV_EWORKSPACE (-3)   /* workspace missing or smaller than the *_workspace_size */
+#define NVFP4KV_EHIP (-4)         /* the HIP runtime reported an error at launch */
+
+#define NVFP4KV_OUT_BF16 0
+#define NVFP4KV_OUT_F32 1
+
+typedef struct nvfp4kv_cache {
+  uint8_t* k_data;  /* [num_pages][num_kv_heads][page_size][head_dim/2]  */
+  uint8_t* k_scale; /* [num_pages][num_kv_heads][page_size][head_dim/16] */
+  uint8_t* v_data;
+  uint8_t* v_scale;
+  float k_global; /* per-tensor scales g (> 0, finite) */
+  float v_global;
+  int32_t num_pages;
+  int32_t page_size;    /* must be 16 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim;     /* must be 128; K and V head sizes are equal ([C] "The two controls are
+                           independent in vLLM" notes the backend requires it) */
+} nvfp4kv_cache_t;
+
+/*
+ * Cache append ([B] "NVFP4 stores 4.5 bits per value before padding", "Decode can win on fewer
+ * bytes read"; [C] "The cache quantizes values during serving"): quantize bf16 K and V, choose
+ * the block scales, pack, and write each token's row to its slot.
+ *   k, v          bf16 [num_tokens][num_kv_heads][head_dim]; heads and dims contiguous, tokens
+ *                 `k_token_stride` / `v_token_stride` elements apart (>= num_kv_heads*head_dim).
+ *   slot_mapping  int64 [num_tokens]; slot < 0 skips the token; slots must be distinct and
+ *                 < num_pages * page_size.
+ * Bytes written are bit-identical to the format definition above.  num_tokens == 0 is a no-op.
+ */
+int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
+                    int64_t k_token_stride, int64_t v_token_stride, const int64_t* slot_mapping,
+                    int32_t num_tokens, void* stream);
+
+/*
+ * Causal paged prefill over the NVFP4 cache with bf16 queries ([A] "Why NVFP4 KV cache A4Q
+ * prefill exists": K and V are unpacked, converted and scaled before BF16 QK and PV; [B] "NVFP4
+ * KV cache prefill vs decode performance").  Append the chunk's K/V first: every key is read
+ * from the cache.
+ *   q             bf16 [total_q][num_qo_heads][head_dim], sequence b owns rows
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *   cu_seqlens_q  int32 [batch+1], kv_lens int32 [batch]; with causal != 0 query row i of a
+ *                 sequence sees keys j <= kv_len - q_len + i (queries at the tail; requires
+ *                 kv_len >= q_len); with causal == 0 every row sees all kv_len keys.
+ *   block_table   int32 [batch][block_table_stride].
+ *   max_q_len, max_kv_len  host-side upper bounds of the device lengths (size the grid).
+ *   query head h reads KV head h / (num_qo_heads / num_kv_heads); the group size must divide
+ *   256 and be <= 64.
+ *   out           [total_q][num_qo_heads][head_dim], bf16 (out_dtype 0) or float32 (1).
+ *   lse           optional float32 [total_q][num_qo_heads]: natural-log sum of exp of the scaled
+ *                 scores (NULL to skip).  A row that sees no key gets out = 0, lse = -inf.
+ *   num_splits    0 = choose automatically; n > 0 splits each row's key range into n parts
+ *                 whose partial results are merged (needs workspace).
+ *   workspace     device scratch of at least paged_prefill_nvfp4_workspace_size(...) bytes
+ *                 (may be NULL when that size is 0).
+ */
+size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
+                                          int32_t max_kv_len, int32_t num_qo_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t num_splits);
+int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_seqlens_q,
+                        const int32_t* kv_lens, const int32_t* block_table,
+                        int32_t block_table_stride, int32_t batch, int32_t total_q,
+                        int32_t max_q_len, int32_t max_kv_len, int32_t num_qo_heads,
+                        float sm_scale, int32_t causal, void* out, int32_t out_dtype, float* lse,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Single-token paged decode ([B] "Decode can win on fewer bytes read": decode reads the growing
+ * cache for one new token after appending its K/V).  Split-KV: each (sequence, KV head, split)
+ * computes a partial softmax over its slice of the cache; a merge combines the partials.
+ *   q        bf16 [batch][num_qo_heads][head_dim]; query b sees all kv_lens[b] keys.
+ *   out      [batch][num_qo_heads][head_dim] bf16 or float32; lse as for prefill.
+ *   num_splits  0 = automatic, else the number of key-range splits per (sequence, KV head).
+ */
+size_t paged_decode_nvfp4_workspace_size(int32_t batch, int32_t max_kv_len, int32_t num_qo_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t num_splits);
+int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* kv_lens,
+                       const int32_t* block_table, int32_t block_table_stride, int32_t batch,
+                       int32_t max_kv_len, int32_t num_qo_heads, float sm_scale, void* out,
+                       int32_t out_dtype, float* lse, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Message describing the last non-zero return on the calling thread ("" if none). */
+const char* nvfp4kv_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t nvfp4kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H */

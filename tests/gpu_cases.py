@@ -1,0 +1,108 @@
+"""Helpers for the GPU tests: upload seeded workloads, run the HIP path through the binding,
+and build the matching oracle cache.  Inputs come only from ``workload``; expected values only
+from ``oracle``."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import attention_nvfp4_quantized_amd as A
+import workload as W
+from oracle import attention as oattn
+from oracle import cache as ocache
+
+DEV = "cuda"
+
+# Output tolerance on attention (float32 output): the bar the path is held to.
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+class GpuPrefillCase:
+    def __init__(self, pc: W.PrefillCase, k_global=1.0, v_global=1.0):
+        self.pc, self.w = pc, pc.w
+        self.cache = A.NVFP4KVCache(pc.layout.num_pages, pc.w.num_kv_heads, k_global=k_global,
+                                    v_global=v_global)
+        self.k, self.v = dev_bf16(pc.k_bits), dev_bf16(pc.v_bits)
+        self.slots = dev(pc.slot_mapping)
+        self.q = dev_bf16(pc.q_bits)
+        self.cu = dev(pc.cu_seqlens_q)
+        self.kv = dev(pc.kv_lens)
+        self.bt = dev(pc.layout.block_table)
+
+    def append(self):
+        A.append(self.cache, self.k, self.v, self.slots)
+
+    def prefill(self, out_dtype=torch.float32, num_splits=0, causal=True, return_lse=False, q=None):
+        r = A.prefill(self.cache, self.q if q is None else q, self.cu, self.kv, self.bt,
+                      self.pc.max_q_len, self.pc.max_kv_len, self.w.sm_scale, causal=causal,
+                      out_dtype=out_dtype, return_lse=return_lse, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return r
+
+    def cache_host(self):
+        c = self.cache
+        return [t.cpu().numpy() for t in (c.k_data, c.k_scale, c.v_data, c.v_scale)]
+
+
+def oracle_cache(pc: W.PrefillCase, seqs=None, k_global=1.0, v_global=1.0) -> ocache.PagedCache:
+    """Oracle cache holding the tokens of the given sequences (all by default)."""
+    c = ocache.PagedCache(pc.layout.num_pages, pc.w.num_kv_heads, k_global=k_global,
+                          v_global=v_global)
+    seqs = range(pc.w.batch) if seqs is None else seqs
+    for b in seqs:
+        s0, s1 = pc.cu_seqlens_kv[b], pc.cu_seqlens_kv[b + 1]
+        c.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1])
+    return c
+
+
+def seq_pages(layout: W.PageLayout, b: int) -> np.ndarray:
+    return layout.block_table[b][: layout.pages_per_seq[b]]
+
+
+def assert_cache_equal(gpu_planes, oc: ocache.PagedCache, pages=None):
+    names = ("k_data", "k_scale", "v_data", "v_scale")
+    for name, g in zip(names, gpu_planes):
+        o = getattr(oc, name)
+        if pages is not None:
+            g, o = g[pages], o[pages]
+        bad = np.argwhere(g != o)
+        assert len(bad) == 0, f"{name}: {len(bad)} bytes differ, first at {bad[0].tolist()}"
+
+
+def attention_error(gpu: np.ndarray, ref: np.ndarray):
+    m = ~np.isnan(ref)
+    d = np.abs(gpu.astype(np.float64)[m] - ref[m])
+    return float(d.max(initial=0.0)), float(d.mean()) if d.size else 0.0
+
+
+def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS,
+                           mean_abs=MEAN_ABS):
+    assert np.isfinite(gpu[~np.isnan(ref)]).all(), f"{what}: non-finite output"
+    mx, mean = attention_error(gpu, ref)
+    say(f"  {what}: max-abs {mx:.3e} mean-abs {mean:.3e} over {int((~np.isnan(ref)).sum())} values")
+    assert mx <= max_abs and mean <= mean_abs, f"{what}: max-abs {mx:.3e}, mean-abs {mean:.3e}"
+
+
+def oracle_prefill(pc: W.PrefillCase, oc: ocache.PagedCache, rows=None, causal=True):
+    return oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
+                         pc.w.sm_scale, causal=causal, rows=rows)
+
+
+def rows_of(pc: W.PrefillCase, seqs) -> np.ndarray:
+    return np.concatenate([np.arange(pc.cu_seqlens_q[b], pc.cu_seqlens_q[b + 1]) for b in seqs])

@@ -1,0 +1,144 @@
+"""The C-ABI library: it loads, exports what the header declares, and rejects bad arguments
+from the host side (CPU only: every case here returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_nvfp4_quantized_amd as A
+from attention_nvfp4_quantized_amd.binding import CacheDesc, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ("nvfp4_kv_append", "paged_prefill_nvfp4", "paged_decode_nvfp4",
+              "paged_prefill_nvfp4_workspace_size", "paged_decode_nvfp4_workspace_size",
+              "nvfp4kv_last_error", "nvfp4kv_version"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(A.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert load_library().nvfp4kv_version() == 100
+
+
+def _desc(**over):
+    d = dict(k_data=16, k_scale=16, v_data=16, v_scale=16, k_global=1.0, v_global=1.0,
+             num_pages=4, page_size=16, num_kv_heads=8, head_dim=128)
+    d.update(over)
+    return CacheDesc(**d)
+
+
+def _err():
+    return load_library().nvfp4kv_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(head_dim=64), -2, "head_dim"),
+    (dict(page_size=32), -2, "page_size"),
+    (dict(k_data=None), -1, "NULL"),
+    (dict(num_kv_heads=0), -1, "num_kv_heads"),
+    (dict(k_global=0.0), -1, "global"),
+    (dict(v_global=float("inf")), -1, "global"),
+])
+def test_append_rejects_bad_cache(over, code, needle):
+    lib = load_library()
+    d = _desc(**over)
+    rc = lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 16, 4, None)
+    assert rc == code and needle in _err()
+
+
+def test_append_rejects_short_stride_and_null_inputs():
+    lib = load_library()
+    d = _desc()
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 512, 1024, 16, 4, None) == -1
+    assert lib.nvfp4_kv_append(ctypes.byref(d), None, 16, 1024, 1024, 16, 4, None) == -1
+    assert lib.nvfp4_kv_append(None, 16, 16, 1024, 1024, 16, 4, None) == -1
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 16, 0, None) == 0
+    assert _err() == ""
+
+
+def _prefill(lib, d, **kw):
+    a = dict(q=16, cu=16, kv=16, bt=16, bts=8, batch=1, total_q=16, max_q=16, max_kv=128,
+             hq=32, sm=0.088, causal=1, out=16, odt=0, lse=None, splits=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.paged_prefill_nvfp4(ctypes.byref(d), a["q"], a["cu"], a["kv"], a["bt"], a["bts"],
+                                   a["batch"], a["total_q"], a["max_q"], a["max_kv"], a["hq"],
+                                   a["sm"], a["causal"], a["out"], a["odt"], a["lse"], a["splits"],
+                                   a["ws"], a["wsb"], None)
+
+
+def test_prefill_argument_checks():
+    lib = load_library()
+    d = _desc()
+    assert _prefill(lib, d, hq=30) == -1 and "multiple" in _err()
+    assert _prefill(lib, d, hq=8 * 3) == -2  # group 3 does not divide 256
+    assert _prefill(lib, d, bts=2) == -1 and "block_table_stride" in _err()
+    assert _prefill(lib, d, sm=0.0) == -1
+    assert _prefill(lib, d, odt=7) == -1
+    assert _prefill(lib, d, q=None) == -1
+    assert _prefill(lib, d, q=8) == -1 and "aligned" in _err()
+    assert _prefill(lib, _desc(head_dim=96)) == -2
+    assert _prefill(lib, d, total_q=0) == 0  # empty problem: no launch
+    assert _prefill(lib, d, batch=0) == 0
+
+
+def test_prefill_split_needs_workspace():
+    lib = load_library()
+    d = _desc()
+    need = A.prefill_workspace_size(1, 16, 16, 128, 32, 8, num_splits=4)
+    assert need == 4 * 16 * 32 * 129 * 4
+    assert _prefill(lib, d, splits=4) == -3 and str(need) in _err()
+    assert _prefill(lib, d, splits=4, ws=16, wsb=need - 1) == -3
+
+
+def test_decode_argument_checks():
+    lib = load_library()
+    d = _desc()
+
+    def dec(**kw):
+        a = dict(q=16, kv=16, bt=16, bts=2048, batch=64, max_kv=32768, hq=32, sm=0.088, out=16,
+                 odt=0, lse=None, splits=0, ws=16, wsb=1 << 40)
+        a.update(kw)
+        return lib.paged_decode_nvfp4(ctypes.byref(d), a["q"], a["kv"], a["bt"], a["bts"], a["batch"],
+                                      a["max_kv"], a["hq"], a["sm"], a["out"], a["odt"], a["lse"],
+                                      a["splits"], a["ws"], a["wsb"], None)
+    assert dec(hq=8 * 32) == -2 and "16" in _err()
+    assert dec(bts=100) == -1
+    assert dec(ws=None) == -3
+    assert dec(wsb=100) == -3
+    assert dec(max_kv=0) == -1
+    assert dec(batch=0) == 0
+    need = A.decode_workspace_size(64, 32768, 32, 8, num_splits=8)
+    assert need == 8 * 64 * 32 * 129 * 4
+
+
+def test_workspace_sizes_follow_split_policy():
+    # long single-sequence prefill: enough workgroups without splitting
+    assert A.prefill_workspace_size(1, 16384, 16384, 16384, 32, 8) == 0
+    # short tails over long caches split the key range
+    assert A.prefill_workspace_size(8, 128, 16, 16384, 32, 8) > 0
+    assert A.decode_workspace_size(64, 32768, 32, 8) > 0
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    import attention_nvfp4_quantized_amd.binding as B
+    saved = B._lib
+    try:
+        B._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            B.load_library(str(tmp_path / "missing.so"))
+    finally:
+        B._lib = saved

@@ -1,0 +1,147 @@
+"""GPU parity: the HIP path against the oracle on the five seeded workloads.
+
+Cache bytes and scales must be bit-exact; attention output (float32 and bf16) must be within
+max-abs 1e-2 and mean-abs 1e-3 of the float64 oracle.  Large workloads run at full size in the
+launch configuration the benchmark times, and are checked on sampled rows / sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_nvfp4_quantized_amd as A
+import workload as W
+from oracle import attention as oattn
+from oracle import cache as ocache
+from gpu_cases import (GpuPrefillCase, assert_attention_close, assert_cache_equal, dev, dev_bf16,
+                       oracle_cache, oracle_prefill, rows_of, say, seq_pages)
+
+pytestmark = pytest.mark.gpu
+
+FULL16K_ROWS = np.array([0, 1, 2, 15, 16, 31, 32, 63, 64, 65, 127, 128, 1000, 4095, 4096, 8191,
+                         8192, 12345, 16255, 16256, 16319, 16320, 16382, 16383])
+
+
+def _bf16_of(x32: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(x32, np.float32).view(np.uint32)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail128", "full16k"])
+def test_append_bit_exact(name):
+    w = W.get(name)
+    say(f"[append] {name}")
+    pc = W.prefill_case(w)
+    g = GpuPrefillCase(pc)
+    g.append()
+    torch.cuda.synchronize()
+    assert_cache_equal(g.cache_host(), oracle_cache(pc))
+
+
+def test_append_bit_exact_tail16_sampled_sequences():
+    w = W.get("tail16")
+    say("[append] tail16 (sequences 0 and 5)")
+    pc = W.prefill_case(w)
+    g = GpuPrefillCase(pc)
+    g.append()
+    torch.cuda.synchronize()
+    seqs = [0, 5]
+    pages = np.concatenate([seq_pages(pc.layout, b) for b in seqs])
+    assert_cache_equal(g.cache_host(), oracle_cache(pc, seqs), pages=pages)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail128"])
+def test_prefill_parity_all_rows(name):
+    w = W.get(name)
+    say(f"[prefill] {name}")
+    pc = W.prefill_case(w)
+    g = GpuPrefillCase(pc)
+    g.append()
+    o32, lse = g.prefill(torch.float32, return_lse=True)
+    o16 = g.prefill(torch.bfloat16)
+    ref, ref_lse = oracle_prefill(pc, oracle_cache(pc))
+    o32n = o32.cpu().numpy()
+    assert_attention_close(o32n, ref, f"{name} fp32")
+    assert_attention_close(o16.float().cpu().numpy(), ref, f"{name} bf16")
+    assert np.array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16), _bf16_of(o32n))
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)
+
+
+def test_prefill_parity_full16k_sampled_rows():
+    w = W.get("full16k")
+    say("[prefill] full16k sampled rows")
+    pc = W.prefill_case(w)
+    g = GpuPrefillCase(pc)
+    g.append()
+    o32 = g.prefill(torch.float32).cpu().numpy()
+    o16 = g.prefill(torch.bfloat16).float().cpu().numpy()
+    ref, _ = oracle_prefill(pc, oracle_cache(pc), rows=FULL16K_ROWS)
+    assert_attention_close(o32, ref, "full16k fp32")
+    assert_attention_close(o16, ref, "full16k bf16")
+
+
+def test_prefill_parity_tail16_sampled_sequences():
+    w = W.get("tail16")
+    say("[prefill] tail16 sequences 0, 5")
+    pc = W.prefill_case(w)
+    g = GpuPrefillCase(pc)
+    g.append()
+    o32 = g.prefill(torch.float32).cpu().numpy()
+    seqs = [0, 5]
+    ref, _ = oracle_prefill(pc, oracle_cache(pc, seqs), rows=rows_of(pc, seqs))
+    assert_attention_close(o32, ref, "tail16 fp32")
+
+
+class DecodeRun:
+    """The decode workload at full size: 64 sequences, 64 steps of (append 64 tokens, decode).
+
+    Sampled sequences carry their seeded K/V; the others keep zero K/V, which changes none of
+    the sampled outputs (sequences are independent) and none of the launch shapes."""
+
+    def __init__(self, sampled, check_steps):
+        self.w = W.get("decode")
+        self.dc = W.decode_case(self.w)
+        lay, w = self.dc.layout, self.w
+        self.cache = A.NVFP4KVCache(lay.num_pages, w.num_kv_heads)
+        self.kv_bits = {b: self.dc.seq_kv(b) for b in sampled}
+        for b, (k, v) in self.kv_bits.items():
+            n = int(self.dc.init_lens[b]) - 1
+            A.append(self.cache, dev_bf16(k[:n]), dev_bf16(v[:n]), dev(lay.slots(b, np.arange(n))))
+        q_all = self.dc.step_q()
+        bt = dev(lay.block_table)
+        self.out = {}
+        max_kv = int(self.dc.init_lens.max()) + w.decode_steps - 1
+        zeros = np.zeros((w.batch, w.num_kv_heads, w.head_dim), np.uint16)
+        for t in range(w.decode_steps):
+            kb, vb = zeros.copy(), zeros.copy()
+            for b, (k, v) in self.kv_bits.items():
+                kb[b], vb[b] = k[int(self.dc.init_lens[b]) - 1 + t], v[int(self.dc.init_lens[b]) - 1 + t]
+            A.append(self.cache, dev_bf16(kb), dev_bf16(vb), dev(self.dc.step_slots(t)))
+            o = A.decode(self.cache, dev_bf16(q_all[t]), dev(self.dc.step_kv_lens(t)), bt, max_kv,
+                         w.sm_scale, out_dtype=torch.float32)
+            if t in check_steps:
+                self.out[t] = o.cpu().numpy()
+        torch.cuda.synchronize()
+        self.q_all = q_all
+
+    def oracle(self, steps, sampled):
+        """Oracle outputs at the given steps; its cache holds every token up to the last step
+        (a decode at step t reads only the first L_b + t of them)."""
+        lay = self.dc.layout
+        oc = ocache.PagedCache(lay.num_pages, self.w.num_kv_heads)
+        for b in sampled:
+            k, v = self.kv_bits[b]
+            n = int(self.dc.init_lens[b]) + max(steps)
+            oc.append(k[:n], v[:n], lay.slots(b, np.arange(n)))
+        return {t: oattn.decode(oc, self.q_all[t], self.dc.step_kv_lens(t), lay.block_table,
+                                self.w.sm_scale, seqs=sampled)[0] for t in steps}
+
+
+def test_decode_parity_full_size_sampled_sequences():
+    w = W.get("decode")
+    lens = np.asarray(w.kv_lens)
+    sampled = [int(lens.argmin()), int(lens.argmax())]
+    say(f"[decode] 64 steps, sampled sequences {sampled} (L = {lens[sampled].tolist()})")
+    run = DecodeRun(sampled, check_steps=(0, 63))
+    refs = run.oracle((0, 63), sampled)
+    for t in (0, 63):
+        assert_attention_close(run.out[t], refs[t], f"decode step {t}")
