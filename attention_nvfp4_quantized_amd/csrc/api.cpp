@@ -54,7 +54,8 @@ int check_cache(const nvfp4kv_cache_t* c) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int kDecodeChunkMin = 512;  // keys per decode slice, lower bound
+constexpr int kDecodeChunkMin = 512;   // keys per decode slice, lower bound
+constexpr int kDecodeChunkMax = 8192;  // keys per decode slice, upper bound
 
 // Waves per prefill workgroup: 8 when the query tile is long enough, else the fewest 32-column
 // waves that hold every (row, head) column of the longest sequence.
@@ -83,7 +84,9 @@ int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, in
     const long cap = std::max(1, (max_kv_len + kDecodeChunkMin - 1) / kDecodeChunkMin);
     s = (int)std::min(want, cap);
   }
-  // slice length: a multiple of 4 waves x 32 tokens covering max_kv_len in s slices
+  // slice length: a multiple of 4 waves x 32 tokens covering max_kv_len in s slices, and at
+  // most 4 x 2048 keys (each wavefront keeps its slice's page ids in two registers)
+  s = std::max(s, (max_kv_len + kDecodeChunkMax - 1) / kDecodeChunkMax);
   int c = (max_kv_len + s - 1) / s;
   c = ((c + 127) / 128) * 128;
   if (c < 128) c = 128;

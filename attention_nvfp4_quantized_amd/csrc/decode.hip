@@ -33,26 +33,120 @@ struct DecodeRegs {
   uint32_t ks[2], vs[2];
 };
 
-__device__ __forceinline__ void decode_load(const DecodeParams& p, const int32_t* bt_row, int hk,
-                                            int kv_len, int k, int lane, DecodeRegs& r) {
+// Page id of the wave-relative page index `pi` (uniform, < 128) from the two page-id registers.
+__device__ __forceinline__ int page_at(int pt0, int pt1, int pi) {
+  return __builtin_amdgcn_readlane(pi < 64 ? pt0 : pt1, pi & 63);
+}
+
+// Issue the loads of the 32 tokens starting at k (two 16-token groups, one page each).  Loads
+// are unconditional: a group past the wave's range re-reads the range's last group (an L2 hit),
+// and tokens past the range are zeroed at use time, so every step issues the same 8 loads and
+// the wait counts stay exact.
+__device__ __forceinline__ void decode_load(const DecodeParams& p, int hk, int wk0, int wk1,
+                                            int pt0, int pt1, int k, int lane, DecodeRegs& r) {
+  const int last_group = (wk1 - 1) & ~15;
+  const int q4 = lane >> 4;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int first = k + 16 * g;  // wave-uniform; 16-aligned, so one page per group
-    const int tok = first + (lane & 15);
-    r.kd[g] = r.vd[g] = u32x4{0u, 0u, 0u, 0u};
-    r.ks[g] = r.vs[g] = 0u;
-    if (first < kv_len) {
-      const int page = bt_row[uniform(first >> 4)];
-      if (tok < kv_len) {
-        const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (tok & 15);
-        const int q4 = lane >> 4;
-        r.kd[g] = *(const u32x4*)(p.k_data + row * kRowBytes + 16 * q4);
-        r.vd[g] = *(const u32x4*)(p.v_data + row * kRowBytes + 16 * q4);
-        r.ks[g] = *(const uint16_t*)(p.k_scale + row * kScaleBytes + 2 * q4);
-        r.vs[g] = *(const uint16_t*)(p.v_scale + row * kScaleBytes + 2 * q4);
-      }
-    }
+    const int first = min(k + 16 * g, last_group);
+    const int page = page_at(pt0, pt1, (first - wk0) >> 4);
+    const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (lane & 15);
+    r.kd[g] = *(const u32x4*)(p.k_data + row * kRowBytes + 16 * q4);
+    r.vd[g] = *(const u32x4*)(p.v_data + row * kRowBytes + 16 * q4);
+    // the dword holding this lane's two scale bytes (shifted into place at use time)
+    r.ks[g] = *(const uint32_t*)(p.k_scale + row * kScaleBytes + 4 * (q4 >> 1));
+    r.vs[g] = *(const uint32_t*)(p.v_scale + row * kScaleBytes + 4 * (q4 >> 1));
   }
+}
+
+struct DecodeState {
+  f32x4 acc_o[8];
+  float m_used;
+  float l_part;
+};
+
+// One 32-token step: scores, V staging, online softmax, PV.
+__device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1, int lane,
+                                            const bf16x8 (&qf)[4], float cs, char* stage,
+                                            DecodeState& st) {
+  const int q4 = lane >> 4;
+  const int t16 = lane & 15;
+  f32x4 sc[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const bool ok = k + 16 * g + t16 < wk1;  // this lane's token is in range
+    const uint32_t ksw = ok ? r.ks[g] >> (16 * (q4 & 1)) : 0u;
+    const float s0 = e4m3_byte<0>(ksw);
+    const float s1 = e4m3_byte<1>(ksw);
+    f32x4 a = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint32_t o4[4];
+      dequant8(r.kd[g][kk], kk < 2 ? s0 : s1, o4);
+      a = mfma16(__builtin_bit_cast(bf16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
+    }
+    sc[g] = a;
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const bool ok = k + 16 * g + t16 < wk1;
+    const uint32_t vsw = ok ? r.vs[g] >> (16 * (q4 & 1)) : 0u;
+    const float s0 = e4m3_byte<0>(vsw);
+    const float s1 = e4m3_byte<1>(vsw);
+    uint32_t o[16];
+    dequant8(r.vd[g][0], s0, o + 0);
+    dequant8(r.vd[g][1], s0, o + 4);
+    dequant8(r.vd[g][2], s1, o + 8);
+    dequant8(r.vd[g][3], s1, o + 12);
+    char* dst = stage + (16 * g + t16) * kDecVStride + 64 * q4;
+    *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
+    *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
+    *(u32x4*)(dst + 32) = u32x4{o[8], o[9], o[10], o[11]};
+    *(u32x4*)(dst + 48) = u32x4{o[12], o[13], o[14], o[15]};
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k + 16 * g + 4 * q4 + j >= wk1) sc[g][j] = kNegInf;
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[0][j], sc[1][j]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = pair32_max(mx) * cs;
+  if (wave_any(mx > st.m_used + 8.0f)) {
+    const float m_new = fmaxf(st.m_used, mx);
+    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(st.m_used - m_new);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
+    st.l_part *= alpha;
+    st.m_used = m_new;
+  }
+  const float mref = (st.m_used == kNegInf) ? 0.0f : st.m_used;
+  bf16x8 pb;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = fast_exp2(fmaf(sc[g][j], cs, -mref));
+      st.l_part += e;
+      pb[4 * g + j] = (__bf16)e;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const char* lo_row = stage + (4 * q4 + (t16 >> 2)) * kDecVStride + 8 * (t16 & 3);
+  const char* hi_row = lo_row + 16 * kDecVStride;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const i16x4 lo = lds_read_tr16(lo_row + 32 * mb);
+    const i16x4 hi = lds_read_tr16(hi_row + 32 * mb);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    st.acc_o[mb] = mfma16(a, pb, st.acc_o[mb]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
@@ -79,7 +173,7 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
   }
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = uniform(threadIdx.x >> 6);
   const int col = lane & 15;
   const int q4 = lane >> 4;
   const bool colv = col < G;
@@ -94,118 +188,63 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
     }
   }
 
-  const int per_wave = p.chunk / kDecWaves;
+  const int per_wave = p.chunk / kDecWaves;  // <= 2048: 128 page ids, two per lane
   const int wk0 = key_begin + w * per_wave;
   const int wk1 = min(kv_len, wk0 + per_wave);
   const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
   const float cs = p.score_scale;
   char* stage = smem + w * kDecStageBytes;
 
-  f32x4 acc_o[8];
+  DecodeState st;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc_o[i] = f32x4{};
-  float m_used = kNegInf;
-  float l_part = 0.0f;
+  for (int i = 0; i < 8; ++i) st.acc_o[i] = f32x4{};
+  st.m_used = kNegInf;
+  st.l_part = 0.0f;
 
-  DecodeRegs cur;
-  if (wk0 < wk1) decode_load(p, bt_row, hk, kv_len, wk0, lane, cur);
-  for (int k = wk0; k < wk1; k += kDecStep) {
-    DecodeRegs nxt;
-    const bool more = k + kDecStep < wk1;
-    if (more) decode_load(p, bt_row, hk, kv_len, k + kDecStep, lane, nxt);
-
-    // ---- scores for 2 x 16 tokens
-    f32x4 sc[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float s0 = e4m3_byte<0>(cur.ks[g]);
-      const float s1 = e4m3_byte<1>(cur.ks[g]);
-      f32x4 a = f32x4{};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t o4[4];
-        dequant8(cur.kd[g][kk], kk < 2 ? s0 : s1, o4);
-        a = mfma16(__builtin_bit_cast(bf16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
-      }
-      sc[g] = a;
+  if (wk0 < wk1) {
+    const int seq_pages = (kv_len + 15) >> 4;
+    const int pb0 = (wk0 >> 4) + lane;
+    const int pt0_ld = pb0 < seq_pages ? bt_row[pb0] : 0;
+    const int pt1_ld = pb0 + 64 < seq_pages ? bt_row[pb0 + 64] : 0;
+    // Copy the page ids through a register move the compiler cannot see into: the loop then
+    // reads plain registers instead of load results it would re-wait for on every iteration.
+    int pt0, pt1;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(pt0) : "v"(pt0_ld));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(pt1) : "v"(pt1_ld));
+    // four register sets in rotation: the loads of three 32-token steps are in flight while
+    // the fourth is consumed
+    DecodeRegs r0, r1, r2, r3;
+    decode_load(p, hk, wk0, wk1, pt0, pt1, wk0, lane, r0);
+    decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + kDecStep, lane, r1);
+    decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + 2 * kDecStep, lane, r2);
+#define NVFP4KV_DECODE_STAGE(CUR, NXT, OFF)                                          \
+  {                                                                                  \
+    decode_load(p, hk, wk0, wk1, pt0, pt1, k + (OFF) + 3 * kDecStep, lane, NXT);    \
+    __builtin_amdgcn_sched_barrier(0);                                               \
+    decode_step(CUR, k + (OFF), wk1, lane, qf, cs, stage, st);                       \
+    __builtin_amdgcn_sched_barrier(0);                                               \
+  }
+    for (int k = wk0; k < wk1; k += 4 * kDecStep) {
+      NVFP4KV_DECODE_STAGE(r0, r3, 0)
+      NVFP4KV_DECODE_STAGE(r1, r0, kDecStep)
+      NVFP4KV_DECODE_STAGE(r2, r1, 2 * kDecStep)
+      NVFP4KV_DECODE_STAGE(r3, r2, 3 * kDecStep)
     }
-    // ---- stage V (bf16, row-major [token][d]) for the transposed operand reads
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float s0 = e4m3_byte<0>(cur.vs[g]);
-      const float s1 = e4m3_byte<1>(cur.vs[g]);
-      uint32_t o[16];
-      dequant8(cur.vd[g][0], s0, o + 0);
-      dequant8(cur.vd[g][1], s0, o + 4);
-      dequant8(cur.vd[g][2], s1, o + 8);
-      dequant8(cur.vd[g][3], s1, o + 12);
-      char* dst = stage + (16 * g + (lane & 15)) * kDecVStride + 64 * q4;
-      *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
-      *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
-      *(u32x4*)(dst + 32) = u32x4{o[8], o[9], o[10], o[11]};
-      *(u32x4*)(dst + 48) = u32x4{o[12], o[13], o[14], o[15]};
-    }
-    // ---- mask tokens past the wave's range, then online softmax
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (k + 16 * g + 4 * q4 + j >= wk1) sc[g][j] = kNegInf;
-    float mx = kNegInf;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[0][j], sc[1][j]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = pair32_max(mx) * cs;
-    if (wave_any(mx > m_used + 8.0f)) {
-      const float m_new = fmaxf(m_used, mx);
-      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc_o[i] *= alpha;
-      l_part *= alpha;
-      m_used = m_new;
-    }
-    const float mref = (m_used == kNegInf) ? 0.0f : m_used;
-    bf16x8 pb;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float e = fast_exp2(fmaf(sc[g][j], cs, -mref));
-        l_part += e;
-        pb[4 * g + j] = (__bf16)e;
-      }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- O^T += V^T P^T over 8 blocks of 16 head-dim values
-    const int t16 = lane & 15;
-    const char* lo_row = stage + (4 * q4 + (t16 >> 2)) * kDecVStride + 8 * (t16 & 3);
-    const char* hi_row = lo_row + 16 * kDecVStride;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const i16x4 lo = lds_read_tr16(lo_row + 32 * mb);
-      const i16x4 hi = lds_read_tr16(hi_row + 32 * mb);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc_o[mb] = mfma16(a, pb, acc_o[mb]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (more) cur = nxt;
+#undef NVFP4KV_DECODE_STAGE
   }
 
   // ---- combine the four wavefronts in LDS
-  float l_tot = l_part + __shfl_xor(l_part, 16);
+  float l_tot = st.l_part + __shfl_xor(st.l_part, 16);
   l_tot = pair32_sum(l_tot);
   __syncthreads();  // every wavefront is done with its V stage
   float* red_o = (float*)smem;  // [wave][16 columns][128]
   if (q4 == 0) {
-    red_m[w][col] = m_used;
+    red_m[w][col] = st.m_used;
     red_l[w][col] = l_tot;
   }
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb)
-    *(f32x4*)(red_o + (w * 16 + col) * kHeadDim + 16 * mb + 4 * q4) = acc_o[mb];
+    *(f32x4*)(red_o + (w * 16 + col) * kHeadDim + 16 * mb + 4 * q4) = st.acc_o[mb];
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
     const int c = idx >> 7;

@@ -1,0 +1,276 @@
+"""Benchmark of the NVFP4 paged-KV attention path on one MI355X.
+
+Headline step (timed K times after W warm-ups): append of the 16,384-token chunk into the NVFP4
+cache followed by the causal paged prefill over it (32 query / 8 KV heads, head_dim 128, page
+size 16, shuffled pages).  ``value`` is the prefill's algorithmic FLOP rate over the whole step.
+The same run also times the 64-step decode loop (batch 64, 16K..32K cached tokens; each step
+appends one token per sequence and decodes) and reports decode microseconds per call and HBM
+GB/s, and times the CPU oracle on a bounded sample of the prefill workload.
+
+Algorithmic work (nothing masked, padded or re-read is counted):
+  prefill FLOP = 4 * head_dim * Hq * sum_b [q_b (kv_b - q_b) + q_b (q_b + 1) / 2]
+  decode bytes = sum_b kv_len_b * Hkv * 144 (K and V: 64 packed + 8 scale bytes each)
+                 + Q and O (2 bytes * Hq * head_dim each per sequence)
+  append bytes = tokens * Hkv * (2 * 2 * head_dim read + 2 * 72 written)
+Peaks: bf16 dense MFMA 2.5 PFLOP/s; HBM 8 TB/s (MI355X published figures).
+
+Prints one JSON line.  Inputs are resident in HBM before any timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workload as W  # noqa: E402
+
+METRIC = "NVFP4-KV causal prefill TFLOP/s @16K; decode µs/call & HBM GB/s"
+PEAK_MFMA_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "prefill_full16k_pmc.json")
+PREFILL_SOURCES = ["prefill.hip", "device_common.hpp", "kernel_params.hpp"]
+
+
+def prefill_flops(q_lens, kv_lens, hq, d=128) -> float:
+    pairs = sum(q * (kv - q) + q * (q + 1) // 2 for q, kv in zip(q_lens, kv_lens))
+    return 4.0 * d * hq * pairs
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "attention_nvfp4_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_units: float):
+    """HBM bytes per prefill launch from the committed rocprofv3 counter summary, or None when
+    the prefill kernel sources changed since the counters were taken."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        pmc = json.load(f)
+    if pmc.get("source_hash") != source_hash(PREFILL_SOURCES):
+        return None
+    return pmc["hbm_bytes_per_launch"]
+
+
+def bf16_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def run_prefill(args, torch, A):
+    w = W.get("full16k")
+    pc = W.prefill_case(w)
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    k, v = bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch)
+    slots = torch.from_numpy(pc.slot_mapping).cuda()
+    q = bf16_dev(pc.q_bits, torch)
+    cu = torch.from_numpy(pc.cu_seqlens_q).cuda()
+    kv = torch.from_numpy(pc.kv_lens).cuda()
+    bt = torch.from_numpy(pc.layout.block_table).cuda()
+    out = torch.empty((pc.total_q, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = A.prefill_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
+                                        w.num_qo_heads, w.num_kv_heads)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        A.append(cache, k, v, slots)
+        if ev is not None:
+            ev[1].record()
+        A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out,
+                  workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    append_bytes = pc.k_bits.shape[0] * w.num_kv_heads * (2 * 2 * 128 + 2 * 72)
+    return dict(w=w, pc=pc, flops=flops, ms_step=ms_step, append_ms=append_ms,
+                prefill_ms=prefill_ms, append_bytes=append_bytes)
+
+
+def run_decode(args, torch, A):
+    w = W.get("decode")
+    dc = W.decode_case(w)
+    lay = dc.layout
+    cache = A.NVFP4KVCache(lay.num_pages, w.num_kv_heads)
+    steps = w.decode_steps
+    step_k = np.zeros((steps, w.batch, w.num_kv_heads, 128), np.uint16)
+    step_v = np.zeros_like(step_k)
+
+    def fill(b):
+        kb, vb = dc.seq_kv(b)
+        n = int(dc.init_lens[b]) - 1
+        step_k[:, b], step_v[:, b] = kb[n:n + steps], vb[n:n + steps]
+        return b, kb[:n], vb[:n], lay.slots(b, np.arange(n))
+
+    workers = min(16, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        for b, kb, vb, sl in ex.map(fill, range(w.batch)):
+            A.append(cache, bf16_dev(kb, torch), bf16_dev(vb, torch), torch.from_numpy(sl).cuda())
+    torch.cuda.synchronize()
+    qs = bf16_dev(dc.step_q(), torch)
+    ks, vs = bf16_dev(step_k, torch), bf16_dev(step_v, torch)
+    slots = torch.from_numpy(np.stack([dc.step_slots(t) for t in range(steps)])).cuda()
+    lens_np = np.stack([dc.step_kv_lens(t) for t in range(steps)])
+    lens = torch.from_numpy(lens_np).cuda()
+    bt = torch.from_numpy(lay.block_table).cuda()
+    max_kv = int(lens_np.max())
+    out = torch.empty((w.batch, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(A.decode_workspace_size(w.batch, max_kv, w.num_qo_heads, w.num_kv_heads),
+                     dtype=torch.uint8, device="cuda")
+
+    def loop(ev=None):
+        for t in range(steps):
+            if ev is not None:
+                ev[t][0].record()
+            A.append(cache, ks[t], vs[t], slots[t])
+            if ev is not None:
+                ev[t][1].record()
+            A.decode(cache, qs[t], lens[t], bt, max_kv, w.sm_scale, out=out, workspace=ws)
+            if ev is not None:
+                ev[t][2].record()
+
+    # the warm-up pass rewrites the same step tokens, so the timed pass sees identical caches
+    loop()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    loop(ev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bytes_per_step = (lens_np.sum(axis=1) * w.num_kv_heads * 144
+                      + 2 * 2 * w.batch * w.num_qo_heads * 128).astype(np.float64)
+    gbps = float(bytes_per_step.sum() / (dec_ms.sum() * 1e-3) / 1e9)
+    append_bytes = w.batch * w.num_kv_heads * (2 * 2 * 128 + 2 * 72)
+    return {
+        "workload": "decode", "batch": w.batch, "steps": steps,
+        "kv_len_min": int(lens_np.min()), "kv_len_max": int(lens_np.max()),
+        "loop_ms": round((t1 - t0) * 1e3, 3),
+        "us_per_call": round(float(dec_ms.mean()) * 1e3, 2),
+        "bytes_per_call": int(bytes_per_step.mean()),
+        "GBps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)},
+        "append_us_per_call": round(float(app_ms.mean()) * 1e3, 2),
+        "append_GBps": round(append_bytes / (app_ms.mean() * 1e-3) / 1e9, 1),
+    }
+
+
+def run_cpu_baseline(pc):
+    """The oracle, untuned, on a bounded sample of the 16K prefill: all 32 heads of 96 query
+    rows spread evenly over the sequence (their visible keys included), after the oracle's
+    append of all 16,384 tokens (timed separately)."""
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    w = pc.w
+    t0 = time.perf_counter()
+    oc = ocache.PagedCache(pc.layout.num_pages, w.num_kv_heads)
+    oc.append(pc.k_bits, pc.v_bits, pc.slot_mapping)
+    t_append = time.perf_counter() - t0
+    rows = np.linspace(0, pc.total_q - 1, 96).round().astype(np.int64)
+    t0 = time.perf_counter()
+    oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table, w.sm_scale,
+                  rows=rows)
+    t_pre = time.perf_counter() - t0
+    flops = 4.0 * 128 * w.num_qo_heads * float((rows + 1).sum())
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / t_pre / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(blas_threads or cores), "host_cores": cores, "kind": "oracle",
+            "sample": "oracle float64 prefill of 96 evenly spaced query rows x 32 heads of the "
+                      "16K causal prefill (%.3g algorithmic FLOP, %.1f s), after the oracle's "
+                      "append of all 16,384 tokens (%.1f s, not in value)" % (flops, t_pre, t_append),
+            "seconds": round(t_pre + t_append, 2)}
+
+
+def copy_calibration(torch, nbytes=1 << 30):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import attention_nvfp4_quantized_amd as A
+    A.load_library()
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    pre = run_prefill(args, torch, A)
+    value = pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12
+    achieved = pre["flops"] / (pre["prefill_ms"] * 1e-3) / 1e12
+    w = pre["w"]
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, K outlier channels x8)",
+        "config": {"workload": "full16k causal prefill + append", "batch": 1, "q_len": 16384,
+                   "kv_len": 16384, "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": 128, "page_size": 16,
+                   "cache": "NVFP4 (E2M1 + E4M3 per 16)", "seed": w.seed},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": measured_traffic(1), "kernel": "nvfp4_prefill_kernel<8>",
+                     "kernel_ms": round(pre["prefill_ms"], 4), "flop_per_launch": pre["flops"]},
+        "append": {"us_per_call": round(pre["append_ms"] * 1e3, 2), "tokens": 16384,
+                   "GBps": round(pre["append_bytes"] / (pre["append_ms"] * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_decode:
+        line["decode"] = run_decode(args, torch, A)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(pre["pc"])
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
