@@ -27,8 +27,8 @@
 namespace nvfp4kv {
 
 constexpr int kTileKeys = 64;
-constexpr int kKStride = 272;  // LDS bytes per K row: 256 + 16 pad (conflict-free b128 reads)
-constexpr int kVStride = 288;  // LDS bytes per V row: 256 + 32 pad (conflict-free transposed reads)
+constexpr int kKStride = 272;  // LDS bytes per K row: 256 + 16 pad (conflict-free 16 B row reads)
+constexpr int kVStride = 320;  // LDS bytes per V row: 256 + 64 pad (conflict-free transposed reads)
 constexpr int kKTileBytes = kTileKeys * kKStride;
 constexpr int kVTileBytes = kTileKeys * kVStride;
 constexpr int kBufBytes = kKTileBytes + kVTileBytes;
@@ -93,8 +93,88 @@ __device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW>& r) {
   }
 }
 
+// S^T (64 keys x this wave's 32 columns) for the K tile in `buf`.
+__device__ __forceinline__ void tile_scores(const char* buf, int lane, const bf16x8 (&qf)[8],
+                                            f32x16& s0, f32x16& s1) {
+  const char* kb = buf + (lane & 31) * kKStride + 16 * (lane >> 5);
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bf16x8 a0 = *(const bf16x8*)(kb + 32 * t);
+    const bf16x8 a1 = *(const bf16x8*)(kb + 32 * kKStride + 32 * t);
+    s0 = mfma32(a0, qf[t], s0);
+    s1 = mfma32(a1, qf[t], s1);
+  }
+}
+
+// Causal / length mask on a tile whose keys start at k0: keys past the column's limit -> -inf.
+__device__ __forceinline__ void tile_mask(f32x16& s0, f32x16& s1, int k0, int lim, int h32) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int key = k0 + 8 * (j >> 2) + 4 * h32 + (j & 3);
+    if (key > lim) s0[j] = kNegInf;
+    if (key + 32 > lim) s1[j] = kNegInf;
+  }
+}
+
+// Running maximum (base 2) and lazy rescale: the reference maximum moves only when a tile's
+// maximum exceeds it by more than 8, which keeps every weight <= 256.
+__device__ __forceinline__ void tile_max_rescale(const f32x16& s0, const f32x16& s1, float cs,
+                                                 float& m_used, float& l_part,
+                                                 f32x16 (&acc_o)[4]) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+  mx = pair32_max(mx) * cs;
+  if (wave_any(mx > m_used + 8.0f)) {
+    const float m_new = fmaxf(m_used, mx);
+    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
+    l_part *= alpha;
+    m_used = m_new;
+  }
+}
+
+// Weights exp2(s * cs - m) as bf16 MFMA B operands; the row sum uses the same bf16 weights.
+__device__ __forceinline__ void tile_probs(const f32x16& s0, const f32x16& s1, float cs,
+                                           float m_used, bf16x8 (&pb)[4], float& l_part) {
+  const float mref = (m_used == kNegInf) ? 0.0f : m_used;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    pb[(j >> 3)][j & 7] = (__bf16)fast_exp2(fmaf(s0[j], cs, -mref));
+    pb[2 + (j >> 3)][j & 7] = (__bf16)fast_exp2(fmaf(s1[j], cs, -mref));
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) l_part = sum_bf16x8(pb[u], l_part);
+}
+
+// O^T += V^T P^T: 4 head-dim blocks x (2 key blocks x 2 k-steps); V^T operands come from the
+// row-major V tile through transposing LDS reads.
+__device__ __forceinline__ void tile_pv(const char* buf, int lane, const bf16x8 (&pb)[4],
+                                        f32x16 (&acc_o)[4]) {
+  const char* vb = buf + kKTileBytes;
+  const int h32 = lane >> 5, g16 = lane >> 4, t16 = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int key0 = 16 * u + 4 * h32 + (t16 >> 2);  // u = 2 * key block + k-step
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d0 = 32 * db + 16 * (g16 & 1) + 4 * (t16 & 3);
+      const i16x4 lo = lds_read_tr16(vb + key0 * kVStride + 2 * d0);
+      const i16x4 hi = lds_read_tr16(vb + (key0 + 8) * kVStride + 2 * d0);
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_o[db] = mfma32(a, pb[u], acc_o[db]);
+    }
+  }
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
+  // One 32-column block per wavefront, two LDS tile buffers: used for short query tiles
+  // (few columns), where the split-KV grid supplies the parallelism.
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
 
   // ---- work item: XCD-major so one KV head's items share an XCD; query tiles longest first.
@@ -127,7 +207,7 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
 
   // ---- this lane's query column
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = uniform(threadIdx.x >> 6);
   const int h32 = lane >> 5;
   const int col = 32 * w + (lane & 31);
   const int pos = pos0 + col / G;
@@ -206,16 +286,8 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
           l_part *= alpha;
           m_used = m_new;
         }
-        const float mref = (m_used == kNegInf) ? 0.0f : m_used;
         bf16x8 pb[4];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e0 = fast_exp2(fmaf(s0[j], cs, -mref));
-          const float e1 = fast_exp2(fmaf(s1[j], cs, -mref));
-          l_part += e0 + e1;
-          pb[(j >> 3)][j & 7] = (__bf16)e0;
-          pb[2 + (j >> 3)][j & 7] = (__bf16)e1;
-        }
+        tile_probs(s0, s1, cs, m_used, pb, l_part);
         // ---- O^T += V^T P^T: 4 d-blocks x (2 key blocks x 2 k-steps)
         const char* vb = buf + kKTileBytes;
 #pragma unroll
@@ -234,6 +306,165 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
       }
       if (more) store_tile<NW>(smem + (((kt + 1 - t_begin) & 1) * kBufBytes), regs);
       __syncthreads();
+    }
+  }
+
+  // ---- epilogue
+  const float l_tot = pair32_sum(l_part);
+  if (!valid) return;
+  const int64_t orow = (int64_t)(q_start + pos) * p.num_qo_heads + head;
+  if (p.num_splits > 1) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float* po = p.part_o + ((int64_t)split * p.total_q * p.num_qo_heads + orow) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * h32;
+        *(f32x4*)(po + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
+                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
+      }
+    if (h32 == 0)
+      p.part_lse[(int64_t)split * p.total_q * p.num_qo_heads + orow] =
+          l_tot > 0.0f ? m_used + __log2f(l_tot) : kNegInf;
+    return;
+  }
+  const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
+  if (p.out_f32) {
+    float* op = (float*)p.out + orow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * h32;
+        *(f32x4*)(op + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
+                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
+      }
+  } else {
+    uint16_t* op = (uint16_t*)p.out + orow * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * h32;
+        *(u32x2*)(op + d) = u32x2{pack_bf16x2(acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv),
+                                  pack_bf16x2(acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv)};
+      }
+  }
+  if (p.lse && h32 == 0) p.lse[orow] = l_tot > 0.0f ? (m_used + __log2f(l_tot)) * kLn2 : kNegInf;
+}
+
+// ---- staggered variant: 8 wavefronts, two anti-phased groups ------------------------------
+//
+// Two wavefronts share each SIMD (waves w and w+4).  Per 64-key tile a wavefront spends about as
+// long in MFMA work (QK, PV) as in VALU work (softmax, dequantization), so the two groups run
+// the same stages in opposite phase:
+//   group 0 (waves 0-3):  QK(kt)   | softmax(kt) | PV(kt) | dequant(kt+2)
+//   group 1 (waves 4-7):  softmax(kt) | PV(kt) | dequant(kt+2) | QK(kt+1)
+// i.e. MFMA-VALU-MFMA-VALU against VALU-MFMA-VALU-MFMA, so one wavefront of a SIMD feeds the
+// matrix core while the other uses the vector ALU.  Group 1 computes the next tile's scores
+// before the tile barrier, so tiles are dequantized two ahead into a third LDS buffer.
+constexpr int kStagWaves = 8;
+
+__global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[3 * kBufBytes];
+
+  // ---- work item: XCD-major so one KV head's items share an XCD; query tiles longest first.
+  const int wg = blockIdx.x;
+  const int item = (wg & 7) * p.items_per_xcd + (wg >> 3);
+  if (item >= p.total_items) return;
+  const int split = item % p.num_splits;
+  int r = item / p.num_splits;
+  const int qt = p.q_tiles - 1 - (r % p.q_tiles);
+  r /= p.q_tiles;
+  const int b = r % p.batch;
+  const int hk = r / p.batch;
+
+  constexpr int kCols = 32 * kStagWaves;
+  const int G = p.group;
+  const int rows_per_tile = kCols / G;
+  const int q_start = p.cu_q[b];
+  const int q_len = p.cu_q[b + 1] - q_start;
+  const int pos0 = qt * rows_per_tile;
+  if (pos0 >= q_len) return;
+  const int kv_len = p.kv_lens[b];
+  const int pos_last = min(q_len, pos0 + rows_per_tile) - 1;
+  const int shift = p.causal ? kv_len - q_len : 0;  // row i sees keys <= i + shift
+  const int lim_tile = p.causal ? shift + pos_last : kv_len - 1;
+  const int n_keys = max(0, min(kv_len, lim_tile + 1));
+  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
+  const int per_split = (n_tiles + p.num_splits - 1) / p.num_splits;
+  const int t_begin = split * per_split;
+  const int t_end = min(n_tiles, t_begin + per_split);
+
+  // ---- this lane's query column
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const bool ahead = w >= 4;  // group 1 scores the next tile before each barrier
+  const int h32 = lane >> 5;
+  const int col = 32 * w + (lane & 31);
+  const int pos = pos0 + col / G;
+  const int head = hk * G + col % G;
+  const bool valid = pos <= pos_last;
+  const int lim = valid ? (p.causal ? shift + pos : kv_len - 1) : -1;
+  const int wpos_first = pos0 + (32 * w) / G;
+  const int wpos_last = pos0 + (32 * w + 31) / G;
+  const bool wave_active = wpos_first <= pos_last;
+  const int wlim_max = !wave_active ? -1 : (p.causal ? shift + min(wpos_last, pos_last) : kv_len - 1);
+  const int wlim_min = (!wave_active || wpos_last > pos_last) ? -1 : (p.causal ? shift + wpos_first : kv_len - 1);
+
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = p.q + ((int64_t)(q_start + (valid ? pos : 0)) * p.num_qo_heads + head) * kHeadDim + 8 * h32;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 v = valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+      qf[t] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
+  float m_used = kNegInf;
+  float l_part = 0.0f;
+  const float cs = p.score_scale;
+  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+
+  if (t_begin < t_end) {
+    TileRegs<kStagWaves> regs;
+    load_tile<kStagWaves>(p, bt_row, hk, kv_len, t_begin, regs);
+    store_tile<kStagWaves>(smem, regs);
+    if (t_begin + 1 < t_end) {
+      load_tile<kStagWaves>(p, bt_row, hk, kv_len, t_begin + 1, regs);
+      store_tile<kStagWaves>(smem + kBufBytes, regs);
+    }
+    __syncthreads();
+    load_tile<kStagWaves>(p, bt_row, hk, kv_len, min(t_begin + 2, t_end - 1), regs);
+
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if (ahead && t_begin * kTileKeys <= wlim_max) tile_scores(smem, lane, qf, s0, s1);
+    int bi = 0;  // buffer of tile kt
+    for (int kt = t_begin; kt < t_end; ++kt) {
+      char* bcur = smem + bi * kBufBytes;
+      char* bnext = smem + (bi == 2 ? 0 : bi + 1) * kBufBytes;
+      char* bfill = smem + (bi == 0 ? 2 : bi - 1) * kBufBytes;  // tile kt+2
+      const int k0 = kt * kTileKeys;
+      if (k0 <= wlim_max) {
+        if (!ahead) tile_scores(bcur, lane, qf, s0, s1);
+        if (k0 + kTileKeys - 1 > wlim_min) tile_mask(s0, s1, k0, lim, h32);
+        tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);
+        bf16x8 pb[4];
+        tile_probs(s0, s1, cs, m_used, pb, l_part);
+        tile_pv(bcur, lane, pb, acc_o);
+      }
+      if (kt + 2 < t_end) {
+        store_tile<kStagWaves>(bfill, regs);
+        load_tile<kStagWaves>(p, bt_row, hk, kv_len, min(kt + 3, t_end - 1), regs);
+      }
+      if (ahead && kt + 1 < t_end && k0 + kTileKeys <= wlim_max) tile_scores(bnext, lane, qf, s0, s1);
+      __syncthreads();
+      bi = bi == 2 ? 0 : bi + 1;
     }
   }
 
@@ -314,7 +545,7 @@ __global__ __launch_bounds__(256) void nvfp4_merge_kernel(MergeParams p) {
 hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream) {
   const dim3 grid((unsigned)(8 * p.items_per_xcd));
   switch (waves) {
-    case 8: hipLaunchKernelGGL(nvfp4_prefill_kernel<8>, grid, dim3(512), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(nvfp4_prefill_staggered_kernel, grid, dim3(512), 0, stream, p); break;
     case 4: hipLaunchKernelGGL(nvfp4_prefill_kernel<4>, grid, dim3(256), 0, stream, p); break;
     case 2: hipLaunchKernelGGL(nvfp4_prefill_kernel<2>, grid, dim3(128), 0, stream, p); break;
     case 1: hipLaunchKernelGGL(nvfp4_prefill_kernel<1>, grid, dim3(64), 0, stream, p); break;

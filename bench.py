@@ -260,7 +260,7 @@ def main():
                    "cache": "NVFP4 (E2M1 + E4M3 per 16)", "seed": w.seed},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": measured_traffic(1), "kernel": "nvfp4_prefill_kernel<8>",
+                     "traffic": measured_traffic(1), "kernel": "nvfp4_prefill_staggered_kernel",
                      "kernel_ms": round(pre["prefill_ms"], 4), "flop_per_launch": pre["flops"]},
         "append": {"us_per_call": round(pre["append_ms"] * 1e3, 2), "tokens": 16384,
                    "GBps": round(pre["append_bytes"] / (pre["append_ms"] * 1e-3) / 1e9, 1)},

@@ -18,6 +18,10 @@ DEV = "cuda"
 # Output tolerance on attention (float32 output): the bar the path is held to.
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
+# log-sum-exp: the kernels sum the bf16-rounded softmax weights (the same weights the PV product
+# uses); each is within a relative 2^-9 of its float value, so the sum is too and its log is
+# within 2^-9 absolute.  Plus float32 rounding of the rest.
+LSE_ATOL = 2.0 ** -9 + 5e-4
 
 
 def say(*a):
@@ -97,6 +101,29 @@ def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, what: str, max_abs=
     mx, mean = attention_error(gpu, ref)
     say(f"  {what}: max-abs {mx:.3e} mean-abs {mean:.3e} over {int((~np.isnan(ref)).sum())} values")
     assert mx <= max_abs and mean <= mean_abs, f"{what}: max-abs {mx:.3e}, mean-abs {mean:.3e}"
+
+
+def _bf16_round(x: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    return (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+
+
+def assert_attention_close_bf16(gpu: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS,
+                                mean_abs=MEAN_ABS):
+    """bf16 outputs: a correctly rounded bf16 value sits up to half an ulp from the float64
+    value (7.8e-3 for |o| in [2, 4)), so the max-abs bar applies to the error beyond that
+    rounding floor |bf16(ref) - ref|; the mean-abs bar applies to the raw error.  The floor is
+    reported, never hidden."""
+    m = ~np.isnan(ref)
+    g, r = gpu.astype(np.float64)[m], ref[m]
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - r)
+    floor = np.abs(_bf16_round(r).astype(np.float64) - r)
+    beyond = (err - floor).max(initial=0.0)
+    say(f"  {what}: max-abs {err.max():.3e} (bf16 floor there {floor[err.argmax()]:.3e}, "
+        f"beyond floor {beyond:.3e}) mean-abs {err.mean():.3e}")
+    assert beyond <= max_abs and err.mean() <= mean_abs, (
+        f"{what}: max-abs beyond the bf16 floor {beyond:.3e}, mean-abs {err.mean():.3e}")
 
 
 def oracle_prefill(pc: W.PrefillCase, oc: ocache.PagedCache, rows=None, causal=True):

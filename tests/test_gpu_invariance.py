@@ -8,7 +8,7 @@ import workload as W
 from oracle import attention as oattn
 from oracle import cache as ocache
 from oracle import codec as ocodec
-from gpu_cases import (GpuPrefillCase, assert_attention_close, assert_cache_equal, dev, dev_bf16,
+from gpu_cases import (LSE_ATOL, GpuPrefillCase, assert_attention_close, assert_cache_equal, dev, dev_bf16,
                        oracle_cache, oracle_prefill, say)
 
 pytestmark = pytest.mark.gpu
@@ -92,7 +92,7 @@ def test_prefill_ragged_batch(causal):
     o, lse = g.prefill(torch.float32, causal=causal, return_lse=True)
     ref, ref_lse = oracle_prefill(pc, oracle_cache(pc), causal=causal)
     assert_attention_close(o.cpu().numpy(), ref, f"ragged causal={causal}")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 2), (16, 1), (64, 2)])
@@ -115,7 +115,7 @@ def test_prefill_split_sweep(splits):
     o, lse = g.prefill(torch.float32, num_splits=splits, return_lse=True)
     ref, ref_lse = oracle_prefill(pc, oracle_cache(pc))
     assert_attention_close(o.cpu().numpy(), ref, f"splits={splits}")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 def test_page_permutation_is_bitwise_invariant():
@@ -196,7 +196,7 @@ def test_decode_shapes_and_splits(hq, hkv, splits):
     oc = oracle_cache(pc)
     ref, ref_lse = oattn.decode(oc, pc.q_bits, pc.kv_lens, pc.layout.block_table, w.sm_scale)
     assert_attention_close(o.cpu().numpy(), ref, f"decode G={hq // hkv} splits={splits}")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=1e-3)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 def test_runs_are_deterministic():
