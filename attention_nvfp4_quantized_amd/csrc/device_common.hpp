@@ -70,11 +70,30 @@ __device__ __forceinline__ void dequant8(uint32_t word, float s, uint32_t out[4]
   out[3] = pack_bf16x2(d[0] * s, d[1] * s);
 }
 
-// Reductions over the lane pair (l, l^32).  (permlane32_swap with the same value in both
-// operands is miscompiled -- both results come back as the partner's value -- so the exchange
-// goes through ds_bpermute.)
-__device__ __forceinline__ float pair32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float pair32_sum(float x) { return x + __shfl_xor(x, 32); }
+// The values of lanes l and l^32, in some order, in every lane (v_permlane32_swap on x and a
+// copy of x).  Written as inline assembly because the compiler's lowering of the builtin reads
+// the first result register for both results.  The s_nop padding covers the VALU-write ->
+// permlane-read and permlane-write -> VALU-read wait states.  All 64 lanes must be active.
+__device__ __forceinline__ f32x2 pair32_values(float x) {
+  float a = x, b;
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 4\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "s_nop 4"
+      : "+v"(a), "=&v"(b));
+  return f32x2{a, b};
+}
+// Reductions over the lane pair (l, l^32); both lanes get the same bits.
+__device__ __forceinline__ float pair32_max(float x) {
+  const f32x2 v = pair32_values(x);
+  return fmaxf(v[0], v[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const f32x2 v = pair32_values(x);
+  return v[0] + v[1];
+}
 
 // acc + the sum of the eight bf16 values of v (four bf16 pair dot products with (1, 1)).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {

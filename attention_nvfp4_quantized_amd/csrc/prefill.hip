@@ -10,7 +10,9 @@
 //    per 64-key tile and amortised over 32 * waves columns.
 //  * Each 64-key tile is loaded packed from HBM (72 B per key and head for each of K and V),
 //    dequantized exactly to bf16 and written to LDS; the next tile's loads are in flight while
-//    the current tile is consumed (two LDS buffers, one barrier per tile).
+//    the current tile is consumed.  K rows are padded to 272 B; V rows are 256 B with their
+//    16-byte slots XOR-swizzled by key, so that both the dequantized writes and the transposing
+//    reads are free of bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA: each lane then holds
 //    16 keys of one query column per 32-key block, so the softmax row reduction is lane-local
 //    plus one permlane32 swap, and P^T is already the B operand of O^T = V^T P^T.  V^T operands
@@ -27,11 +29,20 @@
 namespace nvfp4kv {
 
 constexpr int kTileKeys = 64;
-constexpr int kKStride = 272;  // LDS bytes per K row: 256 + 16 pad (conflict-free 16 B row reads)
-constexpr int kVStride = 320;  // LDS bytes per V row: 256 + 64 pad (conflict-free transposed reads)
+constexpr int kKStride = 272;  // LDS bytes per K row: 256 + 16 pad (conflict-free 16 B accesses)
+constexpr int kVStride = 256;  // LDS bytes per V row, 16-byte slots swizzled by v_offset()
 constexpr int kKTileBytes = kTileKeys * kKStride;
 constexpr int kVTileBytes = kTileKeys * kVStride;
 constexpr int kBufBytes = kKTileBytes + kVTileBytes;
+
+// Byte offset of 16-byte slot `slot` (0..15, i.e. head-dim values 8*slot..8*slot+7) of V row
+// `key` in a V tile.  The slot index is XORed with 5 * (key & 3): the 64-byte granule index and
+// the slot within the granule are both XORed with key & 3.  Then the 16 lanes of a dequantized
+// write (4 keys x 4 quarters, one slot each) hit 16 distinct slots, and the 4 keys of a
+// transposing read (one 64-byte granule each) hit 4 distinct granules.
+__device__ __forceinline__ int v_offset(int key, int slot) {
+  return key * kVStride + 16 * (slot ^ (5 * (key & 3)));
+}
 
 template <int NW>
 struct TileRegs {
@@ -42,30 +53,27 @@ struct TileRegs {
 
 // Load the packed K and V chunks of tile `kt` that this thread dequantizes.  Chunk `it` of the
 // tile: X = it / 256 (K or V), key = (it % 256) / 4, quarter = it % 4 (32 head-dim values).
-// A wavefront's 64 chunks are the 16 keys of one page, so the page id is wave-uniform.
+// A wavefront's 64 chunks are the 16 keys of one page, so the page id is wave-uniform.  Keys at
+// or past kv_len are clamped to the last key: every load is unconditional and reads written
+// cache bytes, and those keys are masked out of the softmax.
 template <int NW>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t* bt_row, int hk,
                                           int kv_len, int kt, TileRegs<NW>& r) {
+  const int last = kv_len - 1;
 #pragma unroll
   for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
     const int it = threadIdx.x + 64 * NW * j;
     const int X = it >> 8;
     const int key = (it & 255) >> 2;
     const int qq = it & 3;
-    const int gkey = kt * kTileKeys + key;
-    const int first_key = uniform(kt * kTileKeys + (((it & 255) >> 2) & ~15));
-    r.data[j] = u32x4{0u, 0u, 0u, 0u};
-    r.scale[j] = 0u;
-    if (first_key < kv_len) {
-      const int page = bt_row[uniform(first_key >> 4)];
-      if (gkey < kv_len) {
-        const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (gkey & 15);
-        const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
-        const uint8_t* sp = (X == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq;
-        r.data[j] = *(const u32x4*)dp;
-        r.scale[j] = *(const uint16_t*)sp;
-      }
-    }
+    const int first = kt * kTileKeys + (key & ~15);
+    const int page = bt_row[uniform(min(first, last) >> 4)];
+    const int gkey = min(kt * kTileKeys + key, last);
+    const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (gkey & 15);
+    const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
+    const uint8_t* sp = (X == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq;
+    r.data[j] = *(const u32x4*)dp;
+    r.scale[j] = *(const uint16_t*)sp;
   }
 }
 
@@ -85,11 +93,18 @@ __device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW>& r) {
     dequant8(r.data[j][1], s0, o + 4);
     dequant8(r.data[j][2], s1, o + 8);
     dequant8(r.data[j][3], s1, o + 12);
-    char* dst = buf + (X == 0 ? key * kKStride : kKTileBytes + key * kVStride) + 64 * qq;
-    *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
-    *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
-    *(u32x4*)(dst + 32) = u32x4{o[8], o[9], o[10], o[11]};
-    *(u32x4*)(dst + 48) = u32x4{o[12], o[13], o[14], o[15]};
+    if (X == 0) {
+      char* dst = buf + key * kKStride + 64 * qq;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        *(u32x4*)(dst + 16 * w) = u32x4{o[4 * w], o[4 * w + 1], o[4 * w + 2], o[4 * w + 3]};
+    } else {
+      char* vt = buf + kKTileBytes;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        *(u32x4*)(vt + v_offset(key, 4 * qq + w)) =
+            u32x4{o[4 * w], o[4 * w + 1], o[4 * w + 2], o[4 * w + 3]};
+    }
   }
 }
 
@@ -123,10 +138,14 @@ __device__ __forceinline__ void tile_mask(f32x16& s0, f32x16& s1, int k0, int li
 __device__ __forceinline__ void tile_max_rescale(const f32x16& s0, const f32x16& s1, float cs,
                                                  float& m_used, float& l_part,
                                                  f32x16 (&acc_o)[4]) {
-  float mx = kNegInf;
+  float ma = fmaxf(s0[0], s0[1]);
+  float mb = fmaxf(s1[0], s1[1]);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
-  mx = pair32_max(mx) * cs;
+  for (int j = 2; j < 16; j += 2) {
+    ma = fmaxf(fmaxf(ma, s0[j]), s0[j + 1]);
+    mb = fmaxf(fmaxf(mb, s1[j]), s1[j + 1]);
+  }
+  const float mx = pair32_max(fmaxf(ma, mb)) * cs;
   if (wave_any(mx > m_used + 8.0f)) {
     const float m_new = fmaxf(m_used, mx);
     const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
@@ -150,20 +169,24 @@ __device__ __forceinline__ void tile_probs(const f32x16& s0, const f32x16& s1, f
   for (int u = 0; u < 4; ++u) l_part = sum_bf16x8(pb[u], l_part);
 }
 
-// O^T += V^T P^T: 4 head-dim blocks x (2 key blocks x 2 k-steps); V^T operands come from the
-// row-major V tile through transposing LDS reads.
+// O^T += V^T P^T: 4 head-dim blocks x (2 key blocks x 2 k-steps).  The V^T operands come from
+// the swizzled row-major V tile through transposing LDS reads: the lane reads 4 values of
+// rows key0 and key0 + 8, with key0 = 16u + 4 h32 + t16/4, at head-dim offset
+// 32 db + 16 (g16 & 1) + 4 (t16 & 3).
 __device__ __forceinline__ void tile_pv(const char* buf, int lane, const bf16x8 (&pb)[4],
                                         f32x16 (&acc_o)[4]) {
-  const char* vb = buf + kKTileBytes;
   const int h32 = lane >> 5, g16 = lane >> 4, t16 = lane & 15;
+  const int k4 = (t16 >> 2) & 3;  // key & 3 of every row this lane reads
+  const int slot_lo = 2 * (g16 & 1) + ((t16 & 3) >> 1);
+  const char* vb = buf + kKTileBytes + (4 * h32 + (t16 >> 2)) * kVStride +
+                   16 * (slot_lo ^ k4) + 8 * (t16 & 1);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int key0 = 16 * u + 4 * h32 + (t16 >> 2);  // u = 2 * key block + k-step
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int d0 = 32 * db + 16 * (g16 & 1) + 4 * (t16 & 3);
-      const i16x4 lo = lds_read_tr16(vb + key0 * kVStride + 2 * d0);
-      const i16x4 hi = lds_read_tr16(vb + (key0 + 8) * kVStride + 2 * d0);
+      const char* pa = vb + 16 * u * kVStride + 64 * (db ^ k4);
+      const i16x4 lo = lds_read_tr16(pa);
+      const i16x4 hi = lds_read_tr16(pa + 8 * kVStride);
       const bf16x8 a = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc_o[db] = mfma32(a, pb[u], acc_o[db]);
@@ -171,172 +194,96 @@ __device__ __forceinline__ void tile_pv(const char* buf, int lane, const bf16x8 
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
-  // One 32-column block per wavefront, two LDS tile buffers: used for short query tiles
-  // (few columns), where the split-KV grid supplies the parallelism.
-  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+// ---- work item and column bookkeeping shared by both kernels ------------------------------
 
-  // ---- work item: XCD-major so one KV head's items share an XCD; query tiles longest first.
+struct PrefillItem {
+  int split, b, hk, q_start, q_len, kv_len, pos0, pos_last, shift, t_begin, t_end;
+};
+
+// Work item of this workgroup: XCD-major so one KV head's items share an XCD; query tiles
+// longest first.  Returns false if the workgroup has no rows.
+__device__ __forceinline__ bool prefill_item(const PrefillParams& p, int cols, PrefillItem& w) {
   const int wg = blockIdx.x;
   const int item = (wg & 7) * p.items_per_xcd + (wg >> 3);
-  if (item >= p.total_items) return;
-  const int split = item % p.num_splits;
+  if (item >= p.total_items) return false;
+  w.split = item % p.num_splits;
   int r = item / p.num_splits;
   const int qt = p.q_tiles - 1 - (r % p.q_tiles);
   r /= p.q_tiles;
-  const int b = r % p.batch;
-  const int hk = r / p.batch;
-
-  constexpr int kCols = 32 * NW;
-  const int G = p.group;
-  const int rows_per_tile = kCols / G;
-  const int q_start = p.cu_q[b];
-  const int q_len = p.cu_q[b + 1] - q_start;
-  const int pos0 = qt * rows_per_tile;
-  if (pos0 >= q_len) return;
-  const int kv_len = p.kv_lens[b];
-  const int pos_last = min(q_len, pos0 + rows_per_tile) - 1;
-  const int shift = p.causal ? kv_len - q_len : 0;  // row i sees keys <= i + shift
-  const int lim_tile = p.causal ? shift + pos_last : kv_len - 1;
-  const int n_keys = max(0, min(kv_len, lim_tile + 1));
+  w.b = r % p.batch;
+  w.hk = r / p.batch;
+  const int rows_per_tile = cols / p.group;
+  w.q_start = p.cu_q[w.b];
+  w.q_len = p.cu_q[w.b + 1] - w.q_start;
+  w.pos0 = qt * rows_per_tile;
+  if (w.pos0 >= w.q_len) return false;
+  w.kv_len = p.kv_lens[w.b];
+  w.pos_last = min(w.q_len, w.pos0 + rows_per_tile) - 1;
+  w.shift = p.causal ? w.kv_len - w.q_len : 0;  // row i sees keys <= i + shift
+  const int lim_tile = p.causal ? w.shift + w.pos_last : w.kv_len - 1;
+  const int n_keys = max(0, min(w.kv_len, lim_tile + 1));
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
   const int per_split = (n_tiles + p.num_splits - 1) / p.num_splits;
-  const int t_begin = split * per_split;
-  const int t_end = min(n_tiles, t_begin + per_split);
+  w.t_begin = w.split * per_split;
+  w.t_end = min(n_tiles, w.t_begin + per_split);
+  return true;
+}
 
-  // ---- this lane's query column
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const int h32 = lane >> 5;
-  const int col = 32 * w + (lane & 31);
-  const int pos = pos0 + col / G;
-  const int head = hk * G + col % G;
-  const bool valid = pos <= pos_last;
-  const int lim = valid ? (p.causal ? shift + pos : kv_len - 1) : -1;
-  // wave-uniform bounds of the keys this wave's rows can see
-  const int wpos_first = pos0 + (32 * w) / G;
-  const int wpos_last = pos0 + (32 * w + 31) / G;
-  const bool wave_active = wpos_first <= pos_last;
-  const int wlim_max = !wave_active ? -1 : (p.causal ? shift + min(wpos_last, pos_last) : kv_len - 1);
-  const int wlim_min = (!wave_active || wpos_last > pos_last) ? -1 : (p.causal ? shift + wpos_first : kv_len - 1);
+// This lane's query column (position, head) and the key limits of the lane and its wavefront.
+struct PrefillCols {
+  int h32, pos, head, lim, wlim_max, wlim_min;
+  bool valid;
+};
 
-  bf16x8 qf[8];
-  {
-    const uint16_t* qp = p.q + ((int64_t)(q_start + (valid ? pos : 0)) * p.num_qo_heads + head) * kHeadDim + 8 * h32;
+__device__ __forceinline__ PrefillCols prefill_cols(const PrefillParams& p, const PrefillItem& w,
+                                                    int wave, int lane) {
+  PrefillCols c;
+  const int G = p.group;
+  c.h32 = lane >> 5;
+  const int col = 32 * wave + (lane & 31);
+  c.pos = w.pos0 + col / G;
+  c.head = w.hk * G + col % G;
+  c.valid = c.pos <= w.pos_last;
+  c.lim = c.valid ? (p.causal ? w.shift + c.pos : w.kv_len - 1) : -1;
+  const int wpos_first = w.pos0 + (32 * wave) / G;
+  const int wpos_last = w.pos0 + (32 * wave + 31) / G;
+  const bool active = wpos_first <= w.pos_last;
+  c.wlim_max = !active ? -1 : (p.causal ? w.shift + min(wpos_last, w.pos_last) : w.kv_len - 1);
+  c.wlim_min = (!active || wpos_last > w.pos_last) ? -1
+                                                   : (p.causal ? w.shift + wpos_first : w.kv_len - 1);
+  return c;
+}
+
+// Q^T operand of this lane's column: 8 k-steps of 16 head-dim values (zero for padding lanes).
+__device__ __forceinline__ void load_q(const PrefillParams& p, const PrefillItem& w,
+                                       const PrefillCols& c, bf16x8 (&qf)[8]) {
+  const uint16_t* qp = p.q + ((int64_t)(w.q_start + (c.valid ? c.pos : 0)) * p.num_qo_heads + c.head) *
+                                 kHeadDim + 8 * c.h32;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      u32x4 v = valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
-      qf[t] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int t = 0; t < 8; ++t) {
+    const u32x4 v = c.valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+    qf[t] = __builtin_bit_cast(bf16x8, v);
   }
+}
 
-  f32x16 acc_o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
-  float m_used = kNegInf;
-  float l_part = 0.0f;
-  const float cs = p.score_scale;
-
-  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
-  const int g16 = lane >> 4;  // 16-lane group
-  const int t16 = lane & 15;
-
-  if (t_begin < t_end) {
-    TileRegs<NW> regs;
-    load_tile<NW>(p, bt_row, hk, kv_len, t_begin, regs);
-    store_tile<NW>(smem, regs);
-    __syncthreads();
-
-    for (int kt = t_begin; kt < t_end; ++kt) {
-      char* buf = smem + ((kt - t_begin) & 1) * kBufBytes;
-      const bool more = kt + 1 < t_end;
-      if (more) load_tile<NW>(p, bt_row, hk, kv_len, kt + 1, regs);
-
-      const int k0 = kt * kTileKeys;
-      if (k0 <= wlim_max) {
-        // ---- S^T = K Q^T for 64 keys x 32 columns
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
-        const char* kb = buf + (lane & 31) * kKStride + 16 * h32;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 a0 = *(const bf16x8*)(kb + 32 * t);
-          const bf16x8 a1 = *(const bf16x8*)(kb + 32 * kKStride + 32 * t);
-          s0 = mfma32(a0, qf[t], s0);
-          s1 = mfma32(a1, qf[t], s1);
-        }
-        if (k0 + kTileKeys - 1 > wlim_min) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + 8 * (j >> 2) + 4 * h32 + (j & 3);
-            if (key > lim) s0[j] = kNegInf;
-            if (key + 32 > lim) s1[j] = kNegInf;
-          }
-        }
-        // ---- online softmax (base 2)
-        float mx = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
-        mx = pair32_max(mx) * cs;
-        if (wave_any(mx > m_used + 8.0f)) {
-          const float m_new = fmaxf(m_used, mx);
-          const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
-          l_part *= alpha;
-          m_used = m_new;
-        }
-        bf16x8 pb[4];
-        tile_probs(s0, s1, cs, m_used, pb, l_part);
-        // ---- O^T += V^T P^T: 4 d-blocks x (2 key blocks x 2 k-steps)
-        const char* vb = buf + kKTileBytes;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int key0 = 16 * u + 4 * h32 + (t16 >> 2);  // u = 2 * mb + ks
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int d0 = 32 * db + 16 * (g16 & 1) + 4 * (t16 & 3);
-            const i16x4 lo = lds_read_tr16(vb + key0 * kVStride + 2 * d0);
-            const i16x4 hi = lds_read_tr16(vb + (key0 + 8) * kVStride + 2 * d0);
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc_o[db] = mfma32(a, pb[u], acc_o[db]);
-          }
-        }
-      }
-      if (more) store_tile<NW>(smem + (((kt + 1 - t_begin) & 1) * kBufBytes), regs);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue
+// Normalise and store this lane's half of its column: O (bf16 or fp32) and the log-sum-exp,
+// or, in split mode, the slice's normalised partial and its base-2 log-sum-exp.
+__device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const PrefillItem& w,
+                                                 const PrefillCols& c, const f32x16 (&acc_o)[4],
+                                                 float m_used, float l_part) {
   const float l_tot = pair32_sum(l_part);
-  if (!valid) return;
-  const int64_t orow = (int64_t)(q_start + pos) * p.num_qo_heads + head;
-  if (p.num_splits > 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* po = p.part_o + ((int64_t)split * p.total_q * p.num_qo_heads + orow) * kHeadDim;
+  if (!c.valid) return;
+  const int64_t orow = (int64_t)(w.q_start + c.pos) * p.num_qo_heads + c.head;
+  const bool split_mode = p.num_splits > 1;
+  const float inv = l_tot > 0.0f ? (split_mode ? 1.0f : p.out_scale) / l_tot : 0.0f;
+  if (split_mode || p.out_f32) {
+    float* op = split_mode ? p.part_o + ((int64_t)w.split * p.total_q * p.num_qo_heads + orow) * kHeadDim
+                           : (float*)p.out + orow * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * h32;
-        *(f32x4*)(po + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
-                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
-      }
-    if (h32 == 0)
-      p.part_lse[(int64_t)split * p.total_q * p.num_qo_heads + orow] =
-          l_tot > 0.0f ? m_used + __log2f(l_tot) : kNegInf;
-    return;
-  }
-  const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
-  if (p.out_f32) {
-    float* op = (float*)p.out + orow * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * h32;
+        const int d = 32 * db + 8 * jg + 4 * c.h32;
         *(f32x4*)(op + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
                                   acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
       }
@@ -346,21 +293,72 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * h32;
+        const int d = 32 * db + 8 * jg + 4 * c.h32;
         *(u32x2*)(op + d) = u32x2{pack_bf16x2(acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv),
                                   pack_bf16x2(acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv)};
       }
   }
-  if (p.lse && h32 == 0) p.lse[orow] = l_tot > 0.0f ? (m_used + __log2f(l_tot)) * kLn2 : kNegInf;
+  if (c.h32 != 0) return;
+  const float lse2 = l_tot > 0.0f ? m_used + __log2f(l_tot) : kNegInf;
+  if (split_mode)
+    p.part_lse[(int64_t)w.split * p.total_q * p.num_qo_heads + orow] = lse2;
+  else if (p.lse)
+    p.lse[orow] = lse2 * kLn2;
 }
 
-// ---- staggered variant: 8 wavefronts, two anti-phased groups ------------------------------
+// ---- narrow kernel: NW wavefronts of 32 columns, two LDS buffers ---------------------------
+// Used for short query tiles (few columns), where the split-KV grid supplies the parallelism.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+  PrefillItem w;
+  if (!prefill_item(p, 32 * NW, w)) return;
+  const int lane = threadIdx.x & 63;
+  const PrefillCols c = prefill_cols(p, w, uniform(threadIdx.x >> 6), lane);
+  bf16x8 qf[8];
+  load_q(p, w, c, qf);
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
+  float m_used = kNegInf;
+  float l_part = 0.0f;
+  const float cs = p.score_scale;
+  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
+
+  if (w.t_begin < w.t_end) {
+    TileRegs<NW> regs;
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, w.t_begin, regs);
+    store_tile<NW>(smem, regs);
+    __syncthreads();
+    for (int kt = w.t_begin; kt < w.t_end; ++kt) {
+      char* buf = smem + ((kt - w.t_begin) & 1) * kBufBytes;
+      const bool more = kt + 1 < w.t_end;
+      if (more) load_tile<NW>(p, bt_row, w.hk, w.kv_len, kt + 1, regs);
+      const int k0 = kt * kTileKeys;
+      if (k0 <= c.wlim_max) {
+        f32x16 s0, s1;
+        tile_scores(buf, lane, qf, s0, s1);
+        if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);
+        tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);
+        bf16x8 pb[4];
+        tile_probs(s0, s1, cs, m_used, pb, l_part);
+        tile_pv(buf, lane, pb, acc_o);
+      }
+      if (more) store_tile<NW>(smem + (((kt + 1 - w.t_begin) & 1) * kBufBytes), regs);
+      __syncthreads();
+    }
+  }
+  prefill_epilogue(p, w, c, acc_o, m_used, l_part);
+}
+
+// ---- staggered kernel: 8 wavefronts, two anti-phased groups --------------------------------
 //
 // Two wavefronts share each SIMD (waves w and w+4).  Per 64-key tile a wavefront spends about as
 // long in MFMA work (QK, PV) as in VALU work (softmax, dequantization), so the two groups run
 // the same stages in opposite phase:
-//   group 0 (waves 0-3):  QK(kt)   | softmax(kt) | PV(kt) | dequant(kt+2)
-//   group 1 (waves 4-7):  softmax(kt) | PV(kt) | dequant(kt+2) | QK(kt+1)
+//   group 0 (waves 0-3):  QK(kt)      | softmax(kt) | PV(kt)        | dequant(kt+2)
+//   group 1 (waves 4-7):  softmax(kt) | PV(kt)      | dequant(kt+2) | QK(kt+1)
 // i.e. MFMA-VALU-MFMA-VALU against VALU-MFMA-VALU-MFMA, so one wavefront of a SIMD feeds the
 // matrix core while the other uses the vector ALU.  Group 1 computes the next tile's scores
 // before the tile barrier, so tiles are dequantized two ahead into a third LDS buffer.
@@ -368,60 +366,14 @@ constexpr int kStagWaves = 8;
 
 __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[3 * kBufBytes];
-
-  // ---- work item: XCD-major so one KV head's items share an XCD; query tiles longest first.
-  const int wg = blockIdx.x;
-  const int item = (wg & 7) * p.items_per_xcd + (wg >> 3);
-  if (item >= p.total_items) return;
-  const int split = item % p.num_splits;
-  int r = item / p.num_splits;
-  const int qt = p.q_tiles - 1 - (r % p.q_tiles);
-  r /= p.q_tiles;
-  const int b = r % p.batch;
-  const int hk = r / p.batch;
-
-  constexpr int kCols = 32 * kStagWaves;
-  const int G = p.group;
-  const int rows_per_tile = kCols / G;
-  const int q_start = p.cu_q[b];
-  const int q_len = p.cu_q[b + 1] - q_start;
-  const int pos0 = qt * rows_per_tile;
-  if (pos0 >= q_len) return;
-  const int kv_len = p.kv_lens[b];
-  const int pos_last = min(q_len, pos0 + rows_per_tile) - 1;
-  const int shift = p.causal ? kv_len - q_len : 0;  // row i sees keys <= i + shift
-  const int lim_tile = p.causal ? shift + pos_last : kv_len - 1;
-  const int n_keys = max(0, min(kv_len, lim_tile + 1));
-  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int per_split = (n_tiles + p.num_splits - 1) / p.num_splits;
-  const int t_begin = split * per_split;
-  const int t_end = min(n_tiles, t_begin + per_split);
-
-  // ---- this lane's query column
+  PrefillItem w;
+  if (!prefill_item(p, 32 * kStagWaves, w)) return;
   const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const bool ahead = w >= 4;  // group 1 scores the next tile before each barrier
-  const int h32 = lane >> 5;
-  const int col = 32 * w + (lane & 31);
-  const int pos = pos0 + col / G;
-  const int head = hk * G + col % G;
-  const bool valid = pos <= pos_last;
-  const int lim = valid ? (p.causal ? shift + pos : kv_len - 1) : -1;
-  const int wpos_first = pos0 + (32 * w) / G;
-  const int wpos_last = pos0 + (32 * w + 31) / G;
-  const bool wave_active = wpos_first <= pos_last;
-  const int wlim_max = !wave_active ? -1 : (p.causal ? shift + min(wpos_last, pos_last) : kv_len - 1);
-  const int wlim_min = (!wave_active || wpos_last > pos_last) ? -1 : (p.causal ? shift + wpos_first : kv_len - 1);
-
+  const int wave = uniform(threadIdx.x >> 6);
+  const bool ahead = wave >= 4;  // group 1 scores the next tile before each barrier
+  const PrefillCols c = prefill_cols(p, w, wave, lane);
   bf16x8 qf[8];
-  {
-    const uint16_t* qp = p.q + ((int64_t)(q_start + (valid ? pos : 0)) * p.num_qo_heads + head) * kHeadDim + 8 * h32;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 v = valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
-      qf[t] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  load_q(p, w, c, qf);
 
   f32x16 acc_o[4];
 #pragma unroll
@@ -429,88 +381,45 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
   float m_used = kNegInf;
   float l_part = 0.0f;
   const float cs = p.score_scale;
-  const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
-  if (t_begin < t_end) {
+  if (w.t_begin < w.t_end) {
     TileRegs<kStagWaves> regs;
-    load_tile<kStagWaves>(p, bt_row, hk, kv_len, t_begin, regs);
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, w.t_begin, regs);
     store_tile<kStagWaves>(smem, regs);
-    if (t_begin + 1 < t_end) {
-      load_tile<kStagWaves>(p, bt_row, hk, kv_len, t_begin + 1, regs);
+    if (w.t_begin + 1 < w.t_end) {
+      load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, w.t_begin + 1, regs);
       store_tile<kStagWaves>(smem + kBufBytes, regs);
     }
     __syncthreads();
-    load_tile<kStagWaves>(p, bt_row, hk, kv_len, min(t_begin + 2, t_end - 1), regs);
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(w.t_begin + 2, w.t_end - 1), regs);
 
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-    if (ahead && t_begin * kTileKeys <= wlim_max) tile_scores(smem, lane, qf, s0, s1);
-    int bi = 0;  // buffer of tile kt
-    for (int kt = t_begin; kt < t_end; ++kt) {
+    if (ahead && w.t_begin * kTileKeys <= c.wlim_max) tile_scores(smem, lane, qf, s0, s1);
+    int bi = 0;  // buffer holding tile kt
+    for (int kt = w.t_begin; kt < w.t_end; ++kt) {
       char* bcur = smem + bi * kBufBytes;
       char* bnext = smem + (bi == 2 ? 0 : bi + 1) * kBufBytes;
-      char* bfill = smem + (bi == 0 ? 2 : bi - 1) * kBufBytes;  // tile kt+2
+      char* bfill = smem + (bi == 0 ? 2 : bi - 1) * kBufBytes;  // receives tile kt+2
       const int k0 = kt * kTileKeys;
-      if (k0 <= wlim_max) {
+      if (k0 <= c.wlim_max) {
         if (!ahead) tile_scores(bcur, lane, qf, s0, s1);
-        if (k0 + kTileKeys - 1 > wlim_min) tile_mask(s0, s1, k0, lim, h32);
+        if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);
         tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);
         bf16x8 pb[4];
         tile_probs(s0, s1, cs, m_used, pb, l_part);
         tile_pv(bcur, lane, pb, acc_o);
       }
-      if (kt + 2 < t_end) {
+      if (kt + 2 < w.t_end) {
         store_tile<kStagWaves>(bfill, regs);
-        load_tile<kStagWaves>(p, bt_row, hk, kv_len, min(kt + 3, t_end - 1), regs);
+        load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(kt + 3, w.t_end - 1), regs);
       }
-      if (ahead && kt + 1 < t_end && k0 + kTileKeys <= wlim_max) tile_scores(bnext, lane, qf, s0, s1);
+      if (ahead && kt + 1 < w.t_end && k0 + kTileKeys <= c.wlim_max) tile_scores(bnext, lane, qf, s0, s1);
       __syncthreads();
       bi = bi == 2 ? 0 : bi + 1;
     }
   }
-
-  // ---- epilogue
-  const float l_tot = pair32_sum(l_part);
-  if (!valid) return;
-  const int64_t orow = (int64_t)(q_start + pos) * p.num_qo_heads + head;
-  if (p.num_splits > 1) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* po = p.part_o + ((int64_t)split * p.total_q * p.num_qo_heads + orow) * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * h32;
-        *(f32x4*)(po + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
-                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
-      }
-    if (h32 == 0)
-      p.part_lse[(int64_t)split * p.total_q * p.num_qo_heads + orow] =
-          l_tot > 0.0f ? m_used + __log2f(l_tot) : kNegInf;
-    return;
-  }
-  const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
-  if (p.out_f32) {
-    float* op = (float*)p.out + orow * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * h32;
-        *(f32x4*)(op + d) = f32x4{acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv,
-                                  acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv};
-      }
-  } else {
-    uint16_t* op = (uint16_t*)p.out + orow * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * h32;
-        *(u32x2*)(op + d) = u32x2{pack_bf16x2(acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv),
-                                  pack_bf16x2(acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv)};
-      }
-  }
-  if (p.lse && h32 == 0) p.lse[orow] = l_tot > 0.0f ? (m_used + __log2f(l_tot)) * kLn2 : kNegInf;
+  prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
 
 // Log-sum-exp merge of split partials: one wavefront per (query row, head); lane l owns
