@@ -13,6 +13,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
@@ -33,6 +35,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // D[4(l/16)+j][l%16] (j = 0..3).
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp16 forms of the same two MFMA shapes (operand layouts as above).
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // E4M3FN scale byte SEL of `word` -> float (exact: the hardware conversion agrees with the
@@ -85,6 +92,39 @@ __device__ __forceinline__ f32x2 pair32_values(float x) {
       : "+v"(a), "=&v"(b));
   return f32x2{a, b};
 }
+// fp16 read-side conversion.  Every NVFP4 value, E2M1 code times E4M3 scale, has at most 5
+// significant bits and a magnitude in [2^-10, 2688], so it is exact as a normal fp16 number.
+
+// Scale bytes 2*HI and 2*HI+1 of `word` -> fp16 pair (exact).
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3_pair_h(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, HI);
+}
+
+// Eight E2M1 codes in `word` (element 0 in the low nibble) times the scale in both halves of
+// s -> four f16x2 words: one conversion and one packed multiply per pair, both exact.
+__device__ __forceinline__ void dequant8_h(uint32_t word, f16x2 s, uint32_t out[4]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * s);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * s);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * s);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s);
+}
+
+// Two floats -> fp16 pair, rounded toward zero (relative error < 2^-10).
+__device__ __forceinline__ f16x2 pack_f16x2_rtz(float lo, float hi) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// acc + the sum of the eight fp16 values of v.
+__device__ __forceinline__ float sum_f16x8(f16x8 v, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
+
 // Reductions over the lane pair (l, l^32); both lanes get the same bits.
 __device__ __forceinline__ float pair32_max(float x) {
   const f32x2 v = pair32_values(x);

@@ -9,11 +9,15 @@
 //    that share the KV head use every dequantized KV tile: the unpack/scale work is paid once
 //    per 64-key tile and amortised over 32 * waves columns.
 //  * Each 64-key tile is loaded packed from HBM (72 B per key and head for each of K and V),
-//    dequantized exactly to bf16 and written to LDS; the next tile's loads are in flight while
-//    the current tile is consumed.  K rows are padded to 272 B; V rows are 256 B with their
+//    dequantized and written to LDS; the packed loads run two tiles ahead of their use.
+//  * The tiles are fp16: every NVFP4 value (E2M1 code times E4M3 scale) is exact in fp16, and
+//    the conversion is one fp4->fp16 convert plus one packed multiply per pair of values.  Q is
+//    converted to fp16 once per workgroup with a per-column power-of-two scale (exact for every
+//    element within 2^32 of the column's largest), folded into the softmax scale; the weights P
+//    are fp16 too (relative error below 2^-10, finer than bf16).  K rows are padded to 272 B; V rows are 256 B with their
 //    16-byte slots XOR-swizzled by key, so that both the dequantized writes and the transposing
 //    reads are free of bank conflicts.
-//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA: each lane then holds
+//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 fp16 MFMA: each lane then holds
 //    16 keys of one query column per 32-key block, so the softmax row reduction is lane-local
 //    plus one permlane32 swap, and P^T is already the B operand of O^T = V^T P^T.  V^T operands
 //    come straight from the row-major V tile through the transposing LDS read.
@@ -49,16 +53,34 @@ struct TileRegs {
   static constexpr int kItems = 512 / (64 * NW);  // 16-byte chunks per thread per tile
   u32x4 data[kItems];
   uint32_t scale[kItems];
+  int32_t page[kItems];  // page ids of the next tile to load (same value in every lane)
 };
 
-// Load the packed K and V chunks of tile `kt` that this thread dequantizes.  Chunk `it` of the
-// tile: X = it / 256 (K or V), key = (it % 256) / 4, quarter = it % 4 (32 head-dim values).
-// A wavefront's 64 chunks are the 16 keys of one page, so the page id is wave-uniform.  Keys at
-// or past kv_len are clamped to the last key: every load is unconditional and reads written
-// cache bytes, and those keys are masked out of the softmax.
+// Chunk `it` of a tile (0..511): X = it / 256 (K or V), key = (it % 256) / 4, quarter = it % 4
+// (32 head-dim values).  A wavefront's 64 chunks are the 16 keys of one page.
+
+// Fetch the page ids of tile `kt` with vector loads (one word, the same in every lane; `vzero`
+// is a zero the compiler cannot see as uniform, which keeps the loads off the scalar path, whose
+// wait would also drain the LDS queue).  Pages past the sequence's last page are clamped to it.
+template <int NW>
+__device__ __forceinline__ void fetch_pages(const int32_t* bt_row, int kv_len, int kt, int vzero,
+                                            TileRegs<NW>& r) {
+  const int last_page = (kv_len - 1) >> 4;
+#pragma unroll
+  for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
+    const int sub = ((threadIdx.x + 64 * NW * j) & 255) >> 6;  // page of the tile, wave-uniform
+    r.page[j] = bt_row[min(4 * kt + sub, last_page) + vzero];
+  }
+}
+
+// Load the packed K and V chunks of tile `kt` that this thread dequantizes, using the page ids
+// fetched for it, then fetch the page ids of tile `kt_next`.  Keys at or past kv_len are clamped
+// to the last key: every load is unconditional and reads written cache bytes, and those keys are
+// masked out of the softmax.
 template <int NW>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t* bt_row, int hk,
-                                          int kv_len, int kt, TileRegs<NW>& r) {
+                                          int kv_len, int kt, int kt_next, int vzero,
+                                          TileRegs<NW>& r) {
   const int last = kv_len - 1;
 #pragma unroll
   for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
@@ -66,8 +88,7 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t*
     const int X = it >> 8;
     const int key = (it & 255) >> 2;
     const int qq = it & 3;
-    const int first = kt * kTileKeys + (key & ~15);
-    const int page = bt_row[uniform(min(first, last) >> 4)];
+    const int page = uniform(r.page[j]);
     const int gkey = min(kt * kTileKeys + key, last);
     const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (gkey & 15);
     const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
@@ -75,51 +96,54 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t*
     r.data[j] = *(const u32x4*)dp;
     r.scale[j] = *(const uint16_t*)sp;
   }
+  fetch_pages<NW>(bt_row, kv_len, kt_next, vzero, r);
 }
 
-// Dequantize the loaded chunks to bf16 and write them to an LDS tile buffer.
+// A zero held in a vector register that the compiler treats as lane-varying.
+__device__ __forceinline__ int opaque_vzero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// Dequantize the loaded chunks to fp16 (exact) and write them to an LDS tile buffer.  The K / V
+// choice is made with selects, not branches, so the tile stages stay one scheduling region.
 template <int NW>
 __device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW>& r) {
 #pragma unroll
   for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
     const int it = threadIdx.x + 64 * NW * j;
-    const int X = it >> 8;
+    const bool is_v = (it >> 8) != 0;
     const int key = (it & 255) >> 2;
     const int qq = it & 3;
-    const float s0 = e4m3_byte<0>(r.scale[j]);
-    const float s1 = e4m3_byte<1>(r.scale[j]);
+    const f16x2 sc = e4m3_pair_h<false>(r.scale[j]);
+    const f16x2 s0 = __builtin_shufflevector(sc, sc, 0, 0);
+    const f16x2 s1 = __builtin_shufflevector(sc, sc, 1, 1);
     uint32_t o[16];
-    dequant8(r.data[j][0], s0, o + 0);
-    dequant8(r.data[j][1], s0, o + 4);
-    dequant8(r.data[j][2], s1, o + 8);
-    dequant8(r.data[j][3], s1, o + 12);
-    if (X == 0) {
-      char* dst = buf + key * kKStride + 64 * qq;
+    dequant8_h(r.data[j][0], s0, o + 0);
+    dequant8_h(r.data[j][1], s0, o + 4);
+    dequant8_h(r.data[j][2], s1, o + 8);
+    dequant8_h(r.data[j][3], s1, o + 12);
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        *(u32x4*)(dst + 16 * w) = u32x4{o[4 * w], o[4 * w + 1], o[4 * w + 2], o[4 * w + 3]};
-    } else {
-      char* vt = buf + kKTileBytes;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        *(u32x4*)(vt + v_offset(key, 4 * qq + w)) =
-            u32x4{o[4 * w], o[4 * w + 1], o[4 * w + 2], o[4 * w + 3]};
+    for (int w = 0; w < 4; ++w) {
+      const int off = is_v ? kKTileBytes + v_offset(key, 4 * qq + w) : key * kKStride + 64 * qq + 16 * w;
+      *(u32x4*)(buf + off) = u32x4{o[4 * w], o[4 * w + 1], o[4 * w + 2], o[4 * w + 3]};
     }
   }
 }
 
 // S^T (64 keys x this wave's 32 columns) for the K tile in `buf`.
-__device__ __forceinline__ void tile_scores(const char* buf, int lane, const bf16x8 (&qf)[8],
+__device__ __forceinline__ void tile_scores(const char* buf, int lane, const f16x8 (&qf)[8],
                                             f32x16& s0, f32x16& s1) {
   const char* kb = buf + (lane & 31) * kKStride + 16 * (lane >> 5);
   s0 = f32x16{};
   s1 = f32x16{};
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const bf16x8 a0 = *(const bf16x8*)(kb + 32 * t);
-    const bf16x8 a1 = *(const bf16x8*)(kb + 32 * kKStride + 32 * t);
-    s0 = mfma32(a0, qf[t], s0);
-    s1 = mfma32(a1, qf[t], s1);
+    const f16x8 a0 = *(const f16x8*)(kb + 32 * t);
+    const f16x8 a1 = *(const f16x8*)(kb + 32 * kKStride + 32 * t);
+    s0 = mfma32h(a0, qf[t], s0);
+    s1 = mfma32h(a1, qf[t], s1);
   }
 }
 
@@ -156,24 +180,29 @@ __device__ __forceinline__ void tile_max_rescale(const f32x16& s0, const f32x16&
   }
 }
 
-// Weights exp2(s * cs - m) as bf16 MFMA B operands; the row sum uses the same bf16 weights.
+// Weights exp2(s * cs - m) as fp16 MFMA B operands (rounded toward zero, relative error below
+// 2^-10); the row sum uses the same fp16 weights.
 __device__ __forceinline__ void tile_probs(const f32x16& s0, const f32x16& s1, float cs,
-                                           float m_used, bf16x8 (&pb)[4], float& l_part) {
+                                           float m_used, f16x8 (&pb)[4], float& l_part) {
   const float mref = (m_used == kNegInf) ? 0.0f : m_used;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    pb[(j >> 3)][j & 7] = (__bf16)fast_exp2(fmaf(s0[j], cs, -mref));
-    pb[2 + (j >> 3)][j & 7] = (__bf16)fast_exp2(fmaf(s1[j], cs, -mref));
+  for (int j = 0; j < 16; j += 2) {
+    const f16x2 a = pack_f16x2_rtz(fast_exp2(fmaf(s0[j], cs, -mref)), fast_exp2(fmaf(s0[j + 1], cs, -mref)));
+    const f16x2 b = pack_f16x2_rtz(fast_exp2(fmaf(s1[j], cs, -mref)), fast_exp2(fmaf(s1[j + 1], cs, -mref)));
+    pb[j >> 3][j & 7] = a[0];
+    pb[j >> 3][(j & 7) + 1] = a[1];
+    pb[2 + (j >> 3)][j & 7] = b[0];
+    pb[2 + (j >> 3)][(j & 7) + 1] = b[1];
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) l_part = sum_bf16x8(pb[u], l_part);
+  for (int u = 0; u < 4; ++u) l_part = sum_f16x8(pb[u], l_part);
 }
 
 // O^T += V^T P^T: 4 head-dim blocks x (2 key blocks x 2 k-steps).  The V^T operands come from
 // the swizzled row-major V tile through transposing LDS reads: the lane reads 4 values of
 // rows key0 and key0 + 8, with key0 = 16u + 4 h32 + t16/4, at head-dim offset
 // 32 db + 16 (g16 & 1) + 4 (t16 & 3).
-__device__ __forceinline__ void tile_pv(const char* buf, int lane, const bf16x8 (&pb)[4],
+__device__ __forceinline__ void tile_pv(const char* buf, int lane, const f16x8 (&pb)[4],
                                         f32x16 (&acc_o)[4]) {
   const int h32 = lane >> 5, g16 = lane >> 4, t16 = lane & 15;
   const int k4 = (t16 >> 2) & 3;  // key & 3 of every row this lane reads
@@ -187,9 +216,9 @@ __device__ __forceinline__ void tile_pv(const char* buf, int lane, const bf16x8 
       const char* pa = vb + 16 * u * kVStride + 64 * (db ^ k4);
       const i16x4 lo = lds_read_tr16(pa);
       const i16x4 hi = lds_read_tr16(pa + 8 * kVStride);
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc_o[db] = mfma32(a, pb[u], acc_o[db]);
+      const f16x8 a = __builtin_bit_cast(
+          f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_o[db] = mfma32h(a, pb[u], acc_o[db]);
     }
   }
 }
@@ -254,16 +283,38 @@ __device__ __forceinline__ PrefillCols prefill_cols(const PrefillParams& p, cons
   return c;
 }
 
-// Q^T operand of this lane's column: 8 k-steps of 16 head-dim values (zero for padding lanes).
-__device__ __forceinline__ void load_q(const PrefillParams& p, const PrefillItem& w,
-                                       const PrefillCols& c, bf16x8 (&qf)[8]) {
+// Q^T operand of this lane's column as fp16: 8 k-steps of 16 head-dim values (zero for padding
+// lanes).  The column is scaled by 2^sh, chosen from its largest |q| (over the lane pair l, l^32)
+// so that the largest lands in [2^15, 2^16): every bf16 element within a factor 2^32 of the
+// largest converts exactly, and smaller ones are below float32 accumulation precision relative
+// to it.  Returns score_scale * 2^-sh, which turns this column's MFMA scores into base-2 logits.
+__device__ __forceinline__ float load_q(const PrefillParams& p, const PrefillItem& w,
+                                        const PrefillCols& c, f16x8 (&qf)[8]) {
   const uint16_t* qp = p.q + ((int64_t)(w.q_start + (c.valid ? c.pos : 0)) * p.num_qo_heads + c.head) *
                                  kHeadDim + 8 * c.h32;
+  u32x4 raw[8];
+  float amax = 0.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const u32x4 v = c.valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
-    qf[t] = __builtin_bit_cast(bf16x8, v);
+    raw[t] = c.valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[t][i] << 16)),
+                               fabsf(__builtin_bit_cast(float, raw[t][i] & 0xFFFF0000u))));
   }
+  amax = pair32_max(amax);
+  const int sh = amax > 0.0f ? min(100, max(-100, 16 - __builtin_amdgcn_frexp_expf(amax))) : 0;
+  const float up = __builtin_ldexpf(1.0f, sh);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 h = pack_f16x2_rtz(__builtin_bit_cast(float, raw[t][i] << 16) * up,
+                                     __builtin_bit_cast(float, raw[t][i] & 0xFFFF0000u) * up);
+      qf[t][2 * i] = h[0];
+      qf[t][2 * i + 1] = h[1];
+    }
+  return p.score_scale * __builtin_ldexpf(1.0f, -sh);
 }
 
 // Normalise and store this lane's half of its column: O (bf16 or fp32) and the log-sum-exp,
@@ -315,33 +366,35 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
   if (!prefill_item(p, 32 * NW, w)) return;
   const int lane = threadIdx.x & 63;
   const PrefillCols c = prefill_cols(p, w, uniform(threadIdx.x >> 6), lane);
-  bf16x8 qf[8];
-  load_q(p, w, c, qf);
+  f16x8 qf[8];
+  const float cs = load_q(p, w, c, qf);
 
   f32x16 acc_o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
   float m_used = kNegInf;
   float l_part = 0.0f;
-  const float cs = p.score_scale;
   const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
   if (w.t_begin < w.t_end) {
+    const int vzero = opaque_vzero();
+    const int t_last = w.t_end - 1;
     TileRegs<NW> regs;
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, w.t_begin, regs);
+    fetch_pages<NW>(bt_row, w.kv_len, w.t_begin, vzero, regs);
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, w.t_begin, min(w.t_begin + 1, t_last), vzero, regs);
     store_tile<NW>(smem, regs);
     __syncthreads();
     for (int kt = w.t_begin; kt < w.t_end; ++kt) {
       char* buf = smem + ((kt - w.t_begin) & 1) * kBufBytes;
       const bool more = kt + 1 < w.t_end;
-      if (more) load_tile<NW>(p, bt_row, w.hk, w.kv_len, kt + 1, regs);
+      if (more) load_tile<NW>(p, bt_row, w.hk, w.kv_len, kt + 1, min(kt + 2, t_last), vzero, regs);
       const int k0 = kt * kTileKeys;
       if (k0 <= c.wlim_max) {
         f32x16 s0, s1;
         tile_scores(buf, lane, qf, s0, s1);
         if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);
         tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);
-        bf16x8 pb[4];
+        f16x8 pb[4];
         tile_probs(s0, s1, cs, m_used, pb, l_part);
         tile_pv(buf, lane, pb, acc_o);
       }
@@ -372,52 +425,72 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
   const int wave = uniform(threadIdx.x >> 6);
   const bool ahead = wave >= 4;  // group 1 scores the next tile before each barrier
   const PrefillCols c = prefill_cols(p, w, wave, lane);
-  bf16x8 qf[8];
-  load_q(p, w, c, qf);
+  f16x8 qf[8];
+  const float cs = load_q(p, w, c, qf);
 
   f32x16 acc_o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
   float m_used = kNegInf;
   float l_part = 0.0f;
-  const float cs = p.score_scale;
   const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
   if (w.t_begin < w.t_end) {
-    TileRegs<kStagWaves> regs;
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, w.t_begin, regs);
-    store_tile<kStagWaves>(smem, regs);
-    if (w.t_begin + 1 < w.t_end) {
-      load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, w.t_begin + 1, regs);
-      store_tile<kStagWaves>(smem + kBufBytes, regs);
-    }
+    // Two register sets take turns: the packed loads of tile kt+4 are issued while tile kt is
+    // consumed, two tiles ahead of their dequantization.  Tile indices are clamped at t_last.
+    const int vzero = opaque_vzero();
+    const int t_last = w.t_end - 1;
+    const int t0 = w.t_begin;
+    TileRegs<kStagWaves> ra, rb;
+    fetch_pages<kStagWaves>(bt_row, w.kv_len, t0, vzero, ra);
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 1, t_last), vzero, ra);
+    store_tile<kStagWaves>(smem, ra);
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 2, t_last), vzero, ra);
+    store_tile<kStagWaves>(smem + kBufBytes, ra);
     __syncthreads();
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(w.t_begin + 2, w.t_end - 1), regs);
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 4, t_last), vzero, ra);
+    fetch_pages<kStagWaves>(bt_row, w.kv_len, min(t0 + 3, t_last), vzero, rb);
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 5, t_last), vzero, rb);
 
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-    if (ahead && w.t_begin * kTileKeys <= c.wlim_max) tile_scores(smem, lane, qf, s0, s1);
+    if (ahead && t0 * kTileKeys <= c.wlim_max) tile_scores(smem, lane, qf, s0, s1);
     int bi = 0;  // buffer holding tile kt
-    for (int kt = w.t_begin; kt < w.t_end; ++kt) {
-      char* bcur = smem + bi * kBufBytes;
-      char* bnext = smem + (bi == 2 ? 0 : bi + 1) * kBufBytes;
-      char* bfill = smem + (bi == 0 ? 2 : bi - 1) * kBufBytes;  // receives tile kt+2
-      const int k0 = kt * kTileKeys;
-      if (k0 <= c.wlim_max) {
-        if (!ahead) tile_scores(bcur, lane, qf, s0, s1);
-        if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);
-        tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);
-        bf16x8 pb[4];
-        tile_probs(s0, s1, cs, m_used, pb, l_part);
-        tile_pv(bcur, lane, pb, acc_o);
-      }
-      if (kt + 2 < w.t_end) {
-        store_tile<kStagWaves>(bfill, regs);
-        load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(kt + 3, w.t_end - 1), regs);
-      }
-      if (ahead && kt + 1 < w.t_end && k0 + kTileKeys <= c.wlim_max) tile_scores(bnext, lane, qf, s0, s1);
-      __syncthreads();
-      bi = bi == 2 ? 0 : bi + 1;
+    // One tile, with register set R holding tile kt+2.  (A macro rather than a lambda: a lambda
+    // capturing the kernel arguments by reference makes the compiler re-load them from memory.)
+#define NVFP4KV_STAG_STEP(KT, R)                                                                   \
+  {                                                                                                \
+    const int kt = (KT);                                                                           \
+    char* bcur = smem + bi * kBufBytes;                                                            \
+    char* bnext = smem + (bi == 2 ? 0 : bi + 1) * kBufBytes;                                       \
+    char* bfill = smem + (bi == 0 ? 2 : bi - 1) * kBufBytes; /* receives tile kt+2 */              \
+    const int k0 = kt * kTileKeys;                                                                 \
+    if (k0 <= c.wlim_max) {                                                                        \
+      if (!ahead) tile_scores(bcur, lane, qf, s0, s1);                                             \
+      if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);                    \
+      tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);                                         \
+      f16x8 pb[4];                                                                                 \
+      tile_probs(s0, s1, cs, m_used, pb, l_part);                                                  \
+      tile_pv(bcur, lane, pb, acc_o);                                                              \
+    }                                                                                              \
+    /* unconditional, so every step has the same loads in flight; past the last tile the */      \
+    /* writes land in a buffer that is not read again */                                           \
+    store_tile<kStagWaves>(bfill, R);                                                              \
+    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 6, t_last),    \
+                          vzero, R);                                                               \
+    if (ahead && kt + 1 < w.t_end && k0 + kTileKeys <= c.wlim_max)                                 \
+      tile_scores(bnext, lane, qf, s0, s1);                                                        \
+    __syncthreads();                                                                               \
+    bi = bi == 2 ? 0 : bi + 1;                                                                     \
+  }
+    // Both halves of the unrolled loop are unconditional, so the loads of the two register sets
+    // are always in flight in the same order and the compiler's wait counts stay partial.
+    int kt2 = t0;
+    for (; kt2 + 1 < w.t_end; kt2 += 2) {
+      NVFP4KV_STAG_STEP(kt2, ra)
+      NVFP4KV_STAG_STEP(kt2 + 1, rb)
     }
+    if (kt2 < w.t_end) NVFP4KV_STAG_STEP(kt2, ra)
+#undef NVFP4KV_STAG_STEP
   }
   prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
