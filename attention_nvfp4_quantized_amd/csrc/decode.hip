@@ -9,9 +9,11 @@
 //    contiguous quarter of the slice in steps of 32 tokens; all query heads of the group ride
 //    along as MFMA columns, so each packed byte is read and converted exactly once.
 //  * K goes from HBM straight into MFMA operand registers: lane l loads 16 bytes of one token
-//    (32 head-dim values) and converts them, scaled, to bf16.  The head-dim order inside each
+//    (32 head-dim values) and converts them, scaled, to fp16 (exact for every NVFP4 value: one
+//    fp4->fp16 convert and one packed multiply per pair).  Q is fp16 with a per-column
+//    power-of-two scale folded into the softmax scale.  The head-dim order inside each
 //    32-wide k-step is permuted identically for K and Q, which leaves the dot products unchanged
-//    and lets every lane use one 16-byte load.  Scores: S^T = K Q^T with 16x16x32 bf16 MFMA.
+//    and lets every lane use one 16-byte load.  Scores: S^T = K Q^T with 16x16x32 fp16 MFMA.
 //  * V is converted the same way into a small per-wavefront LDS stage and read back with the
 //    transposing LDS load as the A operand of O^T = V^T P^T; P^T needs no data movement.
 //  * Online softmax in base 2 with lazy rescaling (refresh when the maximum grows by > 8).
@@ -67,7 +69,7 @@ struct DecodeState {
 
 // One 32-token step: scores, V staging, online softmax, PV.
 __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1, int lane,
-                                            const bf16x8 (&qf)[4], float cs, char* stage,
+                                            const f16x8 (&qf)[4], float cs, char* stage,
                                             DecodeState& st) {
   const int q4 = lane >> 4;
   const int t16 = lane & 15;
@@ -76,14 +78,15 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
   for (int g = 0; g < 2; ++g) {
     const bool ok = k + 16 * g + t16 < wk1;  // this lane's token is in range
     const uint32_t ksw = ok ? r.ks[g] >> (16 * (q4 & 1)) : 0u;
-    const float s0 = e4m3_byte<0>(ksw);
-    const float s1 = e4m3_byte<1>(ksw);
+    const f16x2 sc2 = e4m3_pair_h<false>(ksw);
+    const f16x2 s0 = __builtin_shufflevector(sc2, sc2, 0, 0);
+    const f16x2 s1 = __builtin_shufflevector(sc2, sc2, 1, 1);
     f32x4 a = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint32_t o4[4];
-      dequant8(r.kd[g][kk], kk < 2 ? s0 : s1, o4);
-      a = mfma16(__builtin_bit_cast(bf16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
+      dequant8_h(r.kd[g][kk], kk < 2 ? s0 : s1, o4);
+      a = mfma16h(__builtin_bit_cast(f16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
     }
     sc[g] = a;
   }
@@ -91,13 +94,14 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
   for (int g = 0; g < 2; ++g) {
     const bool ok = k + 16 * g + t16 < wk1;
     const uint32_t vsw = ok ? r.vs[g] >> (16 * (q4 & 1)) : 0u;
-    const float s0 = e4m3_byte<0>(vsw);
-    const float s1 = e4m3_byte<1>(vsw);
+    const f16x2 sc2 = e4m3_pair_h<false>(vsw);
+    const f16x2 s0 = __builtin_shufflevector(sc2, sc2, 0, 0);
+    const f16x2 s1 = __builtin_shufflevector(sc2, sc2, 1, 1);
     uint32_t o[16];
-    dequant8(r.vd[g][0], s0, o + 0);
-    dequant8(r.vd[g][1], s0, o + 4);
-    dequant8(r.vd[g][2], s1, o + 8);
-    dequant8(r.vd[g][3], s1, o + 12);
+    dequant8_h(r.vd[g][0], s0, o + 0);
+    dequant8_h(r.vd[g][1], s0, o + 4);
+    dequant8_h(r.vd[g][2], s1, o + 8);
+    dequant8_h(r.vd[g][3], s1, o + 12);
     char* dst = stage + (16 * g + t16) * kDecVStride + 64 * q4;
     *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
@@ -112,8 +116,7 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[0][j], sc[1][j]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = pair32_max(mx) * cs;
+  mx = pair32_max(pair16_max(mx)) * cs;
   if (wave_any(mx > st.m_used + 8.0f)) {
     const float m_new = fmaxf(st.m_used, mx);
     const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(st.m_used - m_new);
@@ -123,15 +126,19 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
     st.m_used = m_new;
   }
   const float mref = (st.m_used == kNegInf) ? 0.0f : st.m_used;
-  bf16x8 pb;
+  // fp16 weights (rounded toward zero, relative error below 2^-10); the row sum uses the same
+  // rounded weights as the PV product
+  f16x8 pb;
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e = fast_exp2(fmaf(sc[g][j], cs, -mref));
-      st.l_part += e;
-      pb[4 * g + j] = (__bf16)e;
+    for (int j = 0; j < 4; j += 2) {
+      const f16x2 e = pack_f16x2_rtz(fast_exp2(fmaf(sc[g][j], cs, -mref)),
+                                     fast_exp2(fmaf(sc[g][j + 1], cs, -mref)));
+      pb[4 * g + j] = e[0];
+      pb[4 * g + j + 1] = e[1];
     }
+  st.l_part = sum_f16x8(pb, st.l_part);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -141,8 +148,8 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
   for (int mb = 0; mb < 8; ++mb) {
     const i16x4 lo = lds_read_tr16(lo_row + 32 * mb);
     const i16x4 hi = lds_read_tr16(hi_row + 32 * mb);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    st.acc_o[mb] = mfma16(a, pb, st.acc_o[mb]);
+    const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    st.acc_o[mb] = mfma16h(a, pb, st.acc_o[mb]);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -178,21 +185,42 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
   const int q4 = lane >> 4;
   const bool colv = col < G;
 
-  bf16x8 qf[4];
+  // Q^T operand of this lane's column as fp16, scaled by 2^sh chosen from the column's largest
+  // |q| (over the four lanes holding the column) so that the largest lands in [2^15, 2^16):
+  // every bf16 element within a factor 2^32 of it converts exactly.  2^-sh goes into cs.
+  f16x8 qf[4];
+  float cs;
   {
     const uint16_t* qp = p.q + ((int64_t)b * Hq + hk * G + (colv ? col : 0)) * kHeadDim + 32 * q4;
+    u32x4 raw[4];
+    float amax = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 v = colv ? *(const u32x4*)(qp + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      raw[ks] = colv ? *(const u32x4*)(qp + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[ks][i] << 16)),
+                                 fabsf(__builtin_bit_cast(float, raw[ks][i] & 0xFFFF0000u))));
     }
+    amax = pair32_max(pair16_max(amax));
+    const int sh = amax > 0.0f ? min(100, max(-100, 16 - __builtin_amdgcn_frexp_expf(amax))) : 0;
+    const float up = __builtin_ldexpf(1.0f, sh);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2 h = pack_f16x2_rtz(__builtin_bit_cast(float, raw[ks][i] << 16) * up,
+                                       __builtin_bit_cast(float, raw[ks][i] & 0xFFFF0000u) * up);
+        qf[ks][2 * i] = h[0];
+        qf[ks][2 * i + 1] = h[1];
+      }
+    cs = p.score_scale * __builtin_ldexpf(1.0f, -sh);
   }
 
   const int per_wave = p.chunk / kDecWaves;  // <= 2048: 128 page ids, two per lane
   const int wk0 = key_begin + w * per_wave;
   const int wk1 = min(kv_len, wk0 + per_wave);
   const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
-  const float cs = p.score_scale;
   char* stage = smem + w * kDecStageBytes;
 
   DecodeState st;
@@ -234,8 +262,7 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
   }
 
   // ---- combine the four wavefronts in LDS
-  float l_tot = st.l_part + __shfl_xor(st.l_part, 16);
-  l_tot = pair32_sum(l_tot);
+  const float l_tot = pair32_sum(pair16_sum(st.l_part));
   __syncthreads();  // every wavefront is done with its V stage
   float* red_o = (float*)smem;  // [wave][16 columns][128]
   if (q4 == 0) {

@@ -41,6 +41,9 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 // E4M3FN scale byte SEL of `word` -> float (exact: the hardware conversion agrees with the
 // format definition on all 256 codes).
@@ -123,6 +126,27 @@ __device__ __forceinline__ float sum_f16x8(f16x8 v, float acc) {
   acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
   acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
   return acc;
+}
+
+// The values of lanes l and l^16, in some order, in every lane (v_permlane16_swap, as above).
+__device__ __forceinline__ f32x2 pair16_values(float x) {
+  float a = x, b;
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 4\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "s_nop 4"
+      : "+v"(a), "=&v"(b));
+  return f32x2{a, b};
+}
+__device__ __forceinline__ float pair16_max(float x) {
+  const f32x2 v = pair16_values(x);
+  return fmaxf(v[0], v[1]);
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const f32x2 v = pair16_values(x);
+  return v[0] + v[1];
 }
 
 // Reductions over the lane pair (l, l^32); both lanes get the same bits.
