@@ -36,8 +36,11 @@ import workload as W  # noqa: E402
 METRIC = "NVFP4-KV causal prefill TFLOP/s @16K; decode µs/call & HBM GB/s"
 PEAK_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "prefill_full16k_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_full16k_prefill_decode_b64.json")
+PREFILL_KERNEL = "nvfp4_prefill_staggered_kernel"
 PREFILL_SOURCES = ["prefill.hip", "device_common.hpp", "kernel_params.hpp"]
+DECODE_KERNEL = "nvfp4_decode_kernel"
+DECODE_SOURCES = ["decode.hip", "device_common.hpp", "kernel_params.hpp"]
 
 
 def prefill_flops(q_lens, kv_lens, hq, d=128) -> float:
@@ -53,16 +56,19 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_units: float):
-    """HBM bytes per prefill launch from the committed rocprofv3 counter summary, or None when
-    the prefill kernel sources changed since the counters were taken."""
+def measured_traffic(which: str):
+    """HBM bytes per launch of the prefill ("prefill") or decode ("decode") kernel from the
+    committed rocprofv3 counter summary, or None when that kernel's sources changed since the
+    counters were taken."""
     if not os.path.exists(PMC_FILE):
         return None
     with open(PMC_FILE) as f:
         pmc = json.load(f)
-    if pmc.get("source_hash") != source_hash(PREFILL_SOURCES):
+    entry = pmc.get(which)
+    sources = PREFILL_SOURCES if which == "prefill" else DECODE_SOURCES
+    if not entry or entry.get("source_hash") != source_hash(sources):
         return None
-    return pmc["hbm_bytes_per_launch"]
+    return entry["hbm_bytes_per_launch"]
 
 
 def bf16_dev(bits, torch):
@@ -177,7 +183,8 @@ def run_decode(args, torch, A):
         "bytes_per_call": int(bytes_per_step.mean()),
         "GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)},
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic("decode"), "kernel": DECODE_KERNEL},
         "append_us_per_call": round(float(app_ms.mean()) * 1e3, 2),
         "append_GBps": round(append_bytes / (app_ms.mean() * 1e-3) / 1e9, 1),
     }
@@ -260,7 +267,7 @@ def main():
                    "cache": "NVFP4 (E2M1 + E4M3 per 16)", "seed": w.seed},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": measured_traffic(1), "kernel": "nvfp4_prefill_staggered_kernel",
+                     "traffic": measured_traffic("prefill"), "kernel": PREFILL_KERNEL,
                      "kernel_ms": round(pre["prefill_ms"], 4), "flop_per_launch": pre["flops"]},
         "append": {"us_per_call": round(pre["append_ms"] * 1e3, 2), "tokens": 16384,
                    "GBps": round(pre["append_bytes"] / (pre["append_ms"] * 1e-3) / 1e9, 1)},
