@@ -18,9 +18,10 @@ DEV = "cuda"
 # Output tolerance on attention (float32 output): the bar the path is held to.
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
-# log-sum-exp: the kernels sum the bf16-rounded softmax weights (the same weights the PV product
-# uses); each is within a relative 2^-9 of its float value, so the sum is too and its log is
-# within 2^-9 absolute.  Plus float32 rounding of the rest.
+# log-sum-exp: the kernels sum the rounded softmax weights (the same weights the PV product
+# uses: fp16 rounded toward zero, relative error below 2^-10); each is within a relative 2^-9 of
+# its float value, so the sum is too and its log is within 2^-9 absolute.  Plus float32
+# rounding of the rest.
 LSE_ATOL = 2.0 ** -9 + 5e-4
 
 
