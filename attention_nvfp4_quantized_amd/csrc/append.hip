@@ -3,15 +3,22 @@
 // weights", section "The cache quantizes values during serving"; "NVFP4 KV cache prefill vs
 // decode performance", section "NVFP4 stores 4.5 bits per value before padding").
 //
-// One thread owns one 16-value block: it reads 32 contiguous input bytes, writes 8 packed bytes
-// and one scale byte.  Eight consecutive threads cover one 64-byte cache row, so both the loads
-// and the stores are contiguous across a wavefront.  The kernel is bound by HBM traffic.
+// A wavefront covers 16 consecutive tokens of one KV head (K or V): lane l owns the two 16-value
+// blocks 2(l%4), 2(l%4)+1 of token l/4, reading 64 contiguous input bytes and writing 16 packed
+// bytes and 2 scale bytes.  When the 16 tokens fill one page (consecutive slots, as a prefill
+// chunk's are), the wavefront writes a whole 1 KiB page row of packed data and a whole 128-byte
+// line of scales, so no cache line is partially written.  The kernel is bound by HBM traffic.
 //
 // Exactness: the block scale is E4M3 round-to-nearest-even of the correctly rounded float32
 // quotient amax / 6 (saturating at 448), computed with integer operations on the float bits.
-// Element codes come from comparing |y| with the products t * s for the rounding midpoints
-// t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}; each product has at most 7 significant bits, so the
-// comparisons are exact and ties resolve to the even code.  No reciprocal is used.
+// Element codes are E2M1 round-to-nearest-even (saturating at 6) of the exact quotient y / s.
+// The quotient of a bf16 value by an E4M3 scale either equals a rounding midpoint t * s
+// (t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}) exactly or differs from every midpoint by more
+// than 2^-9 relative: y has 8 significant bits and t * s at most 9, so a nonzero difference is
+// at least one unit of the coarser of the two.  The kernel forms q = y * fl32(1/s) (relative
+// error below 2^-22), corrects it once with the exact residual y - q s, which turns every exact
+// midpoint into exactly t, and rounds q to E2M1 with the hardware conversion (ties to even,
+// saturating).  Zeros keep their sign; a zero scale gives signed zeros.
 #include "device_common.hpp"
 #include "kernel_params.hpp"
 
@@ -35,31 +42,10 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne(float q) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-__device__ __forceinline__ uint32_t e2m1_magnitude(float a, float t1, float t2, float t3, float t4,
-                                                   float t5, float t6, float t7) {
-  return (uint32_t)(a > t1) + (uint32_t)(a >= t2) + (uint32_t)(a > t3) + (uint32_t)(a >= t4) +
-         (uint32_t)(a > t5) + (uint32_t)(a >= t6) + (uint32_t)(a > t7);
-}
-
+// Quantize one 16-value block held as 8 bf16 pairs: returns the E4M3 scale code and the
+// packed codes (element 2i in the low nibble of byte i).
 template <bool UNIT_G>
-__global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
-  const int which = blockIdx.y;  // 0 = K, 1 = V
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int H = p.num_kv_heads;
-  const int64_t nblk = (int64_t)p.num_tokens * H * 8;
-  if (idx >= nblk) return;
-  const int blk = (int)(idx & 7);
-  const int64_t th = idx >> 3;
-  const int h = (int)(th % H);
-  const int64_t t = th / H;
-  const int64_t slot = p.slots[t];
-  if (slot < 0) return;
-
-  const uint16_t* src = (which == 0 ? p.k + t * p.k_stride : p.v + t * p.v_stride) +
-                        (int64_t)h * kHeadDim + blk * 16;
-  const u32x4 lo = *(const u32x4*)(src);
-  const u32x4 hi = *(const u32x4*)(src + 8);
-  const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ uint32_t quantize_block(const uint32_t (&w)[8], float g, u32x2& packed) {
   float y[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -67,7 +53,6 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
     y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
   if (!UNIT_G) {
-    const float g = which == 0 ? p.k_global : p.v_global;
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = __fdiv_rn(y[i], g);
   }
@@ -77,28 +62,62 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
 
   const uint32_t sc = e4m3_encode_rne(__fdiv_rn(amax, 6.0f));
   const float s = e4m3_byte<0>(sc);
-  const float t1 = 0.25f * s, t2 = 0.75f * s, t3 = 1.25f * s, t4 = 1.75f * s;
-  const float t5 = 2.5f * s, t6 = 3.5f * s, t7 = 5.0f * s;
-  const uint32_t keep = sc != 0 ? 0x7u : 0x0u;  // a zero scale forces magnitude 0
-  uint32_t packed[2] = {0u, 0u};
+  const float r = sc != 0 ? __fdiv_rn(1.0f, s) : 0.0f;
+  float q[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t sign = __float_as_uint(y[i]) >> 31;
-    const uint32_t mag = e2m1_magnitude(fabsf(y[i]), t1, t2, t3, t4, t5, t6, t7) & keep;
-    packed[i >> 3] |= ((sign << 3) | mag) << (4 * (i & 7));
+    // residual written as -(q0 s - y): for y = -0 the result stays -0 (the code keeps its sign)
+    const float q0 = y[i] * r;
+    q[i] = __builtin_fmaf(-__builtin_fmaf(q0, s, -y[i]), r, q0);
   }
+  uint32_t lo = 0u, hi = 0u;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[0], q[1], 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[2], q[3], 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[4], q[5], 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[6], q[7], 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[8], q[9], 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[10], q[11], 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[12], q[13], 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[14], q[15], 1.0f, 3);
+  packed = u32x2{lo, hi};
+  return sc;
+}
+
+// Grid: x = groups of 64 tokens (4 wavefronts x 16), y = KV head * 2 + (0 for K, 1 for V).
+template <bool UNIT_G>
+__global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
+  const int which = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane >> 2);
+  const int pair = lane & 3;  // blocks 2 * pair, 2 * pair + 1
+  if (t >= p.num_tokens) return;
+  const int64_t slot = p.slots[t];
+  if (slot < 0) return;
+
+  const uint16_t* src = (which == 0 ? p.k + t * p.k_stride : p.v + t * p.v_stride) +
+                        (int64_t)h * kHeadDim + 32 * pair;
+  const u32x4 in0 = *(const u32x4*)(src);
+  const u32x4 in1 = *(const u32x4*)(src + 8);
+  const u32x4 in2 = *(const u32x4*)(src + 16);
+  const u32x4 in3 = *(const u32x4*)(src + 24);
+  const float g = which == 0 ? p.k_global : p.v_global;
+  const uint32_t wa[8] = {in0[0], in0[1], in0[2], in0[3], in1[0], in1[1], in1[2], in1[3]};
+  const uint32_t wb[8] = {in2[0], in2[1], in2[2], in2[3], in3[0], in3[1], in3[2], in3[3]};
+  u32x2 pa, pb;
+  const uint32_t sa = quantize_block<UNIT_G>(wa, g, pa);
+  const uint32_t sb = quantize_block<UNIT_G>(wb, g, pb);
 
   const int64_t page = slot >> 4;
-  const int64_t row = (page * H + h) * kPageSize + (slot & 15);
-  uint8_t* data = (which == 0 ? p.k_data : p.v_data) + row * kRowBytes + blk * 8;
-  uint8_t* scale = (which == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + blk;
-  *(u32x2*)data = u32x2{packed[0], packed[1]};
-  *scale = (uint8_t)sc;
+  const int64_t row = (page * p.num_kv_heads + h) * kPageSize + (slot & 15);
+  uint8_t* data = (which == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * pair;
+  uint8_t* scale = (which == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * pair;
+  *(u32x4*)data = u32x4{pa[0], pa[1], pb[0], pb[1]};
+  *(uint16_t*)scale = (uint16_t)(sa | (sb << 8));
 }
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  const int64_t nblk = (int64_t)p.num_tokens * p.num_kv_heads * 8;
-  const dim3 grid((unsigned)((nblk + 255) / 256), 2);
+  const dim3 grid((unsigned)((p.num_tokens + 63) / 64), (unsigned)(2 * p.num_kv_heads));
   if (p.k_global == 1.0f && p.v_global == 1.0f)
     hipLaunchKernelGGL(nvfp4_append_kernel<true>, grid, dim3(256), 0, stream, p);
   else

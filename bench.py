@@ -190,6 +190,53 @@ def run_decode(args, torch, A):
     }
 
 
+def run_short_prefill(name, torch, A, reps=20, warmup=5):
+    """Prefill-only timing of a short-query workload (tail128: 4 x 128 queries over 2,048 keys;
+    tail16: 8 x 16 queries over 16,384 keys): median µs per call with a 512 MB buffer written
+    between calls (flushing L2 and MALL, so the packed cache comes from HBM) and warm
+    back-to-back, with algorithmic TFLOP/s and GB/s (Q + O + packed KV of every sequence)."""
+    w = W.get(name)
+    pc = W.prefill_case(w)
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    A.append(cache, bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch),
+             torch.from_numpy(pc.slot_mapping).cuda())
+    q = bf16_dev(pc.q_bits, torch)
+    cu = torch.from_numpy(pc.cu_seqlens_q).cuda()
+    kv = torch.from_numpy(pc.kv_lens).cuda()
+    bt = torch.from_numpy(pc.layout.block_table).cuda()
+    out = torch.empty((pc.total_q, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = A.prefill_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
+                                        w.num_qo_heads, w.num_kv_heads)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def call():
+        A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out,
+                  workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    times = {}
+    for mode in ("flushed", "warm"):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            if mode == "flushed":
+                flush.zero_()
+            ev[i][0].record()
+            call()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        times[mode] = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
+    nbytes = float(sum(w.kv_lens) * w.num_kv_heads * 144 + 2 * 2 * pc.total_q * w.num_qo_heads * 128)
+    t = times["flushed"] * 1e-3
+    return {"workload": name, "batch": w.batch, "q_len": int(w.q_lens[0]), "kv_len": int(w.kv_lens[0]),
+            "us_flushed": round(times["flushed"] * 1e3, 2), "us_warm": round(times["warm"] * 1e3, 2),
+            "TFLOPs": round(flops / t / 1e12, 2), "mfma_frac": round(flops / t / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "GBps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4),
+            "flop_per_call": flops, "bytes_per_call": int(nbytes)}
+
+
 def run_cpu_baseline(pc):
     """The oracle, untuned, on a bounded sample of the 16K prefill: all 32 heads of 96 query
     rows spread evenly over the sequence (their visible keys included), after the oracle's
@@ -238,6 +285,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-short", action="store_true", help="skip the tail128 / tail16 prefill timings")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -274,6 +322,8 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = run_decode(args, torch, A)
+    if not args.no_short:
+        line["short_prefill"] = [run_short_prefill(n, torch, A) for n in ("tail128", "tail16")]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(pre["pc"])
     print(json.dumps(line))
