@@ -67,12 +67,18 @@ int prefill_waves(int max_q_len, int group) {
   return 1;
 }
 
-int prefill_splits(int batch, int q_tiles, int num_kv_heads, int max_kv_len, int requested) {
+// Key slices per prefill work item.  Slicing buys parallelism when there are fewer work items
+// than the GPU holds at once (256 CUs x workgroups per CU: one 8-wave workgroup, whose three
+// tile buffers fill most of the LDS, or two narrow ones), but every extra slice writes and
+// re-reads an fp32 partial of the whole output; so slice only up to that occupancy, and keep at
+// least 8 tiles (512 keys) per slice.
+int prefill_splits(int batch, int q_tiles, int num_kv_heads, int max_kv_len, int nw, int requested) {
   if (requested > 0) return requested;
   const long base = (long)batch * q_tiles * num_kv_heads;
-  if (base >= 1024) return 1;
-  const long want = (2048 + base - 1) / base;
-  const long cap = std::max(1, max_kv_len / 256);
+  const long slots = 256L * (nw == 8 ? 1 : 2);
+  if (base >= slots) return 1;
+  const long want = (slots + base - 1) / base;
+  const long cap = std::max(1, max_kv_len / 512);
   return (int)std::max(1L, std::min(want, cap));
 }
 
@@ -144,7 +150,7 @@ size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_
   if (!group_ok(g)) return 0;
   const int nw = prefill_waves(max_q_len, g);
   const int q_tiles = (max_q_len + (32 * nw / g) - 1) / (32 * nw / g);
-  const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, num_splits);
+  const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, nw, num_splits);
   if (s <= 1) return 0;
   return (size_t)s * total_q * num_qo_heads * (head_dim + 1) * sizeof(float);
 }
@@ -179,7 +185,7 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
   const int nw = prefill_waves(max_q_len, g);
   const int rows = 32 * nw / g;
   const int q_tiles = (max_q_len + rows - 1) / rows;
-  const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, num_splits);
+  const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);
   const long items = (long)cache->num_kv_heads * batch * q_tiles * s;
   if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
 

@@ -377,30 +377,52 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
   const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
   if (w.t_begin < w.t_end) {
+    // Three register sets in rotation: the packed loads of tile kt+4 are issued while tile kt is
+    // consumed, so each tile's loads have three tiles of compute to arrive (these short-query
+    // shapes are bound by memory latency).  Tile indices are clamped at t_last; writes past the
+    // last tile land in a buffer that is not read again.
     const int vzero = opaque_vzero();
     const int t_last = w.t_end - 1;
-    TileRegs<NW> regs;
-    fetch_pages<NW>(bt_row, w.kv_len, w.t_begin, vzero, regs);
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, w.t_begin, min(w.t_begin + 1, t_last), vzero, regs);
-    store_tile<NW>(smem, regs);
+    const int t0 = w.t_begin;
+    TileRegs<NW> r0, r1, r2;
+    fetch_pages<NW>(bt_row, w.kv_len, t0, vzero, r0);
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 3, t_last), vzero, r0);
+    fetch_pages<NW>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 4, t_last), vzero, r1);
+    fetch_pages<NW>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 5, t_last), vzero, r2);
+    store_tile<NW>(smem, r0);
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 6, t_last), vzero, r0);
     __syncthreads();
-    for (int kt = w.t_begin; kt < w.t_end; ++kt) {
-      char* buf = smem + ((kt - w.t_begin) & 1) * kBufBytes;
-      const bool more = kt + 1 < w.t_end;
-      if (more) load_tile<NW>(p, bt_row, w.hk, w.kv_len, kt + 1, min(kt + 2, t_last), vzero, regs);
-      const int k0 = kt * kTileKeys;
-      if (k0 <= c.wlim_max) {
-        f32x16 s0, s1;
-        tile_scores(buf, lane, qf, s0, s1);
-        if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);
-        tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);
-        f16x8 pb[4];
-        tile_probs(s0, s1, cs, m_used, pb, l_part);
-        tile_pv(buf, lane, pb, acc_o);
-      }
-      if (more) store_tile<NW>(smem + (((kt + 1 - w.t_begin) & 1) * kBufBytes), regs);
-      __syncthreads();
+    // One tile; register set R holds tile kt+1, which is written to the other buffer and then
+    // reloaded with tile kt+4.
+#define NVFP4KV_NARROW_STEP(KT, R)                                                                 \
+  {                                                                                                \
+    const int kt = (KT);                                                                           \
+    char* buf = smem + ((kt - t0) & 1) * kBufBytes;                                                \
+    const int k0 = kt * kTileKeys;                                                                 \
+    if (k0 <= c.wlim_max) {                                                                        \
+      f32x16 s0, s1;                                                                               \
+      tile_scores(buf, lane, qf, s0, s1);                                                          \
+      if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);                    \
+      tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);                                         \
+      f16x8 pb[4];                                                                                 \
+      tile_probs(s0, s1, cs, m_used, pb, l_part);                                                  \
+      tile_pv(buf, lane, pb, acc_o);                                                               \
+    }                                                                                              \
+    store_tile<NW>(smem + ((kt + 1 - t0) & 1) * kBufBytes, R);                                     \
+    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 7, t_last), vzero, R); \
+    __syncthreads();                                                                               \
+  }
+    int kt3 = t0;
+    for (; kt3 + 2 < w.t_end; kt3 += 3) {
+      NVFP4KV_NARROW_STEP(kt3, r1)
+      NVFP4KV_NARROW_STEP(kt3 + 1, r2)
+      NVFP4KV_NARROW_STEP(kt3 + 2, r0)
     }
+    if (kt3 < w.t_end) NVFP4KV_NARROW_STEP(kt3, r1)
+    if (kt3 + 1 < w.t_end) NVFP4KV_NARROW_STEP(kt3 + 1, r2)
+#undef NVFP4KV_NARROW_STEP
   }
   prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
