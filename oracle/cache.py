@@ -39,15 +39,18 @@ class PagedCache:
     def nbytes(self) -> int:
         return sum(a.nbytes for a in (self.k_data, self.v_data, self.k_scale, self.v_scale))
 
-    def append(self, k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray):
-        """Quantize bf16 K/V ``[T][num_kv_heads][head_dim]`` and write them to their slots."""
+    def append(self, k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray,
+               input_dtype: str = "bf16"):
+        """Quantize bf16 or fp16 K/V ``[T][num_kv_heads][head_dim]`` (bit patterns) and write
+        them to their slots ("NVFP4 KV cache A4Q prefill explained", section "Preserve the
+        capacity and decode case": the writer takes BF16 or FP16 input)."""
         slots = np.asarray(slot_mapping, dtype=np.int64)
         keep = slots >= 0
         page = slots[keep] // self.page_size
         off = slots[keep] % self.page_size
         for bits, data, scale, g in ((k_bits, self.k_data, self.k_scale, self.k_global),
                                      (v_bits, self.v_data, self.v_scale, self.v_global)):
-            codes, sc = codec.quantize(codec.bf16_to_f32(bits), g)
+            codes, sc = codec.quantize(codec.input_to_f32(bits, input_dtype), g)
             data[page, :, off, :] = codec.pack(codes)[keep]
             scale[page, :, off, :] = sc[keep]
 
@@ -56,6 +59,25 @@ class PagedCache:
         (k_data, k_scale, v_data, v_scale), each [n][num_kv_heads][...]."""
         return (self.k_data[pages, :, offsets, :], self.k_scale[pages, :, offsets, :],
                 self.v_data[pages, :, offsets, :], self.v_scale[pages, :, offsets, :])
+
+    def dequant_slots(self, slot_mapping: np.ndarray, out_dtype: str = "bf16"):
+        """The standalone dequantization: rows of the given slots as g * s * e2m1(code),
+        formed in float32 (s * e2m1 is exact there; the product with g rounds once) and rounded
+        to nearest-even in the output type; slots < 0 give zero rows.  Returns (k, v), each
+        [n][num_kv_heads][head_dim] (bit patterns for bf16 / fp16, float32 for f32)."""
+        slots = np.asarray(slot_mapping, dtype=np.int64)
+        keep = slots >= 0
+        page = np.where(keep, slots // self.page_size, 0)
+        off = np.where(keep, slots % self.page_size, 0)
+        out = []
+        for data, scale, g in ((self.k_data, self.k_scale, self.k_global),
+                               (self.v_data, self.v_scale, self.v_global)):
+            codes = codec.unpack(data[page, :, off, :])
+            s = np.repeat(codec.e4m3_value(scale[page, :, off, :]), codec.BLOCK, axis=-1)
+            x = (s * codec.e2m1_value(codes)).astype(np.float32) * np.float32(g)
+            x = np.where(keep[:, None, None], x, np.float32(0)).astype(np.float32)
+            out.append(codec.round_to_dtype(x, out_dtype))
+        return out[0], out[1]
 
     def gather(self, block_table_row: np.ndarray, n: int):
         """Dequantized K and V of positions 0..n-1 of one sequence: float64 [n][H][D]."""

@@ -142,6 +142,35 @@ def dequantize(packed: np.ndarray, scale_codes: np.ndarray, g: float = 1.0) -> n
     return float(g) * s * e2m1_value(codes)
 
 
+def fp16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact value of IEEE binary16 bit patterns, as float32 (every binary16 value is one)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def input_to_f32(bits: np.ndarray, input_dtype: str = "bf16") -> np.ndarray:
+    """Writer input bit patterns (bf16 or fp16) -> their exact float32 values."""
+    if input_dtype == "bf16":
+        return bf16_to_f32(bits)
+    if input_dtype == "fp16":
+        return fp16_to_f32(bits)
+    raise ValueError(f"input dtype {input_dtype!r}")
+
+
+def round_to_dtype(x: np.ndarray, out_dtype: str) -> np.ndarray:
+    """float32 values rounded to nearest-even in bf16 / fp16 (as bit patterns), or kept as
+    float32: the output types of the standalone dequantization."""
+    x = np.asarray(x, dtype=np.float32)
+    if out_dtype == "f32":
+        return x
+    if out_dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    if out_dtype == "bf16":
+        b = x.view(np.uint32).astype(np.uint64)
+        r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+        return r.astype(np.uint16)
+    raise ValueError(f"output dtype {out_dtype!r}")
+
+
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact value of bfloat16 bit patterns, as float32."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)

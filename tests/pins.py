@@ -35,6 +35,41 @@ def bf16_value(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def finite_fp16_patterns() -> np.ndarray:
+    """Every finite IEEE binary16 bit pattern (both signs, both zeros): 63,488 values."""
+    p = np.arange(65536, dtype=np.uint32)
+    return p[((p >> 10) & 0x1F) != 0x1F].astype(np.uint16)
+
+
+def fp16_value_by_fields(bits: np.ndarray) -> np.ndarray:
+    """binary16 value from its fields (sign, 5-bit exponent of bias 15, 10-bit fraction),
+    exact in float64."""
+    b = bits.astype(np.int64)
+    e, m = (b >> 10) & 0x1F, (b & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -24), np.ldexp(1024.0 + m, (e - 25).astype(np.int64)))
+    return np.where((b >> 15) & 1, -mag, mag)
+
+
+def nearest_even_fraction(x: Fraction, grid_exp_min: int, mant_bits: int) -> Fraction:
+    """x rounded to nearest (ties to even significand) in a binary format with `mant_bits`
+    stored fraction bits and least exponent grid_exp_min (no overflow handling)."""
+    if x == 0:
+        return Fraction(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = max(math.floor(math.log2(a)) if a.numerator else 0, grid_exp_min)
+    while Fraction(2) ** e > a and e > grid_exp_min:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, grid_exp_min)
+    ulp = Fraction(2) ** (e - mant_bits)
+    q, r = divmod(a, ulp)
+    if r * 2 > ulp or (r * 2 == ulp and q % 2 == 1):
+        q += 1
+    return sgn * q * ulp
+
+
 # ---------------------------------------------------------------------------------------
 # Formats
 # ---------------------------------------------------------------------------------------
@@ -119,6 +154,83 @@ def check_element_rounding_exhaustive(codec, scale_codes=range(0, 127)):
         exp = threshold_code(y, s)
         bad = np.nonzero(got != exp)[0]
         assert len(bad) == 0, f"scale code {c:#x}: {len(bad)} mismatches, first y={y[bad[0]]!r}"
+
+
+def check_fp16_decode(codec):
+    """The writer's fp16 input decoding against the field definition, every finite pattern."""
+    bits = finite_fp16_patterns()
+    got = codec.fp16_to_f32(bits).astype(np.float64)
+    exp = fp16_value_by_fields(bits)
+    assert np.array_equal(got, exp) and np.array_equal(np.signbit(got), np.signbit(exp))
+
+
+def check_scale_rounding_exhaustive_fp16(codec):
+    """Every positive finite fp16 amax, against exact rational rounding of amax/6."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    amax = fp16_value_by_fields(bits).astype(np.float32)
+    blocks = np.zeros((len(bits), 16), np.float32)
+    blocks[:, 9] = -amax
+    got = codec.block_scale_codes(blocks)[:, 0]
+    table = _fraction_e4m3_table()
+    exp = np.array([expected_scale_code(Fraction(float(a)), table) for a in amax], np.uint8)
+    bad = np.nonzero(got != exp)[0]
+    assert len(bad) == 0, f"{len(bad)} mismatches, first amax={amax[bad[0]]!r}"
+
+
+def check_element_rounding_exhaustive_fp16(codec, scale_codes=range(0, 127)):
+    """All finite fp16 values (both signs) under every E4M3 scale, against the threshold form."""
+    y = fp16_value_by_fields(finite_fp16_patterns())
+    for c in scale_codes:
+        s = float(codec.e4m3_value(c))
+        got = codec.e2m1_encode(y, s)
+        exp = threshold_code(y.astype(np.float32), s)
+        bad = np.nonzero(got != exp)[0]
+        assert len(bad) == 0, f"scale code {c:#x}: {len(bad)} mismatches, first y={y[bad[0]]!r}"
+
+
+def check_round_to_dtype(codec, seed=11):
+    """bf16 / fp16 output rounding against exact rational nearest-even, on random float32 values,
+    exact ties of both formats, subnormal and near-limit values."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(3000) * np.exp(rng.uniform(-20, 12, 3000))).astype(np.float32)
+    ties_bf16 = (((rng.integers(0, 1 << 15, 500) << 16) | 0x8000)).astype(np.uint32).view(np.float32)
+    ties_fp16 = (rng.integers(1, 1 << 10, 500) * 2.0 ** -11 + 1.0) * 2.0 ** rng.integers(-14, 15, 500)
+    extra = np.array([0.0, -0.0, 2.0 ** -25, 3 * 2.0 ** -26, 65504.0, 6e-8, -1e-40], np.float32)
+    x = np.concatenate([x, ties_bf16[np.isfinite(ties_bf16)], ties_fp16.astype(np.float32), extra])
+    got_b = codec.round_to_dtype(x, "bf16")
+    got_h = codec.round_to_dtype(x, "fp16")
+    for xi, gb, gh in zip(x, got_b, got_h):
+        f = Fraction(float(xi))
+        eb = nearest_even_fraction(f, -126, 7)                     # bf16: 7 fraction bits
+        assert Fraction(float(bf16_value(np.array([gb], np.uint16))[0])) == eb, (xi, gb)
+        if abs(f) < 65520:                                          # below fp16 overflow
+            eh = nearest_even_fraction(f, -14, 10)                   # fp16: 10 fraction bits
+            assert Fraction(float(fp16_value_by_fields(np.array([gh], np.uint16))[0])) == eh, (xi, gh)
+
+
+def check_dequant_routes_agree(codec, cache_mod, seed=5):
+    """The standalone dequantization (float32 product, rounded to the output type) equals the
+    float64 read path used by attention, for g = 1 where every value is exact in bf16 and fp16,
+    and slot < 0 gives zero rows."""
+    rng = np.random.default_rng(seed)
+    c = cache_mod.PagedCache(6, 2)
+    x = (rng.standard_normal((40, 2, 128)) * np.exp(rng.uniform(-6, 6, (40, 2, 1)))).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)          # truncation: any bf16 pattern
+    slots = rng.permutation(96)[:40].astype(np.int64)
+    c.append(bits, bits[::-1].copy(), slots)
+    q = np.concatenate([slots, [-1]])
+    for out in ("bf16", "fp16", "f32"):
+        k, v = c.dequant_slots(q, out)
+        for got, data, scale in ((k, c.k_data, c.k_scale), (v, c.v_data, c.v_scale)):
+            ref = codec.dequantize(data[slots // 16, :, slots % 16, :], scale[slots // 16, :, slots % 16, :])
+            if out == "bf16":
+                val = bf16_value(got[:-1])
+            elif out == "fp16":
+                val = fp16_value_by_fields(got[:-1])
+            else:
+                val = got[:-1]
+            assert np.array_equal(np.asarray(val, np.float64), ref), out
+            assert not np.any(np.asarray(got[-1], np.float64)), out
 
 
 def check_worked_block(codec):

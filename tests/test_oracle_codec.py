@@ -22,6 +22,26 @@ def test_element_rounding_exhaustive_vs_threshold_form():
     pins.check_element_rounding_exhaustive(codec)
 
 
+def test_fp16_input_decode():
+    pins.check_fp16_decode(codec)
+
+
+def test_scale_rounding_exhaustive_fp16_inputs():
+    pins.check_scale_rounding_exhaustive_fp16(codec)
+
+
+def test_element_rounding_exhaustive_fp16_inputs():
+    pins.check_element_rounding_exhaustive_fp16(codec)
+
+
+def test_output_rounding_vs_exact_rationals():
+    pins.check_round_to_dtype(codec)
+
+
+def test_dequant_routes_agree():
+    pins.check_dequant_routes_agree(codec, cache)
+
+
 def test_worked_block():
     pins.check_worked_block(codec)
 
@@ -151,3 +171,32 @@ def test_pins_catch_e4m3_bias_8():
     m = _Mutant(e4m3_value=val)
     with pytest.raises(AssertionError):
         pins.check_e4m3_values(m)
+
+
+def test_pins_catch_fp16_exponent_bias_off_by_one():
+    m = _Mutant(fp16_to_f32=lambda b: codec.fp16_to_f32(b) * np.float32(2.0))
+    with pytest.raises(AssertionError):
+        pins.check_fp16_decode(m)
+
+
+def test_pins_catch_truncating_output_rounding():
+    def rnd(x, out):
+        x = np.asarray(x, np.float32)
+        if out == "bf16":
+            return (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation, not nearest-even
+        return codec.round_to_dtype(x, out)
+    m = _Mutant(round_to_dtype=rnd)
+    with pytest.raises(AssertionError):
+        pins.check_round_to_dtype(m)
+
+
+def test_pins_catch_dequant_without_scale():
+    class C(cache.PagedCache):
+        def dequant_slots(self, slot_mapping, out_dtype="bf16"):
+            k, v = super().dequant_slots(slot_mapping, "f32")
+            g = np.where(k != 0, np.sign(k), 0).astype(np.float32)  # drops the block scale
+            return codec.round_to_dtype(g, out_dtype), codec.round_to_dtype(v, out_dtype)
+    import types
+    mod = types.SimpleNamespace(PagedCache=C)
+    with pytest.raises(AssertionError):
+        pins.check_dequant_routes_agree(codec, mod)
