@@ -47,8 +47,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     C = ctypes.POINTER(CacheDesc)
-    lib.nvfp4_kv_append.argtypes = [C, P, P, I64, I64, P, I32, P]
+    lib.nvfp4_kv_append.argtypes = [C, P, P, I64, I64, I32, P, I32, P]
     lib.nvfp4_kv_append.restype = ctypes.c_int
+    lib.nvfp4_kv_dequant.argtypes = [C, P, I32, P, P, I32, P]
+    lib.nvfp4_kv_dequant.restype = ctypes.c_int
     lib.paged_prefill_nvfp4_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
     lib.paged_prefill_nvfp4_workspace_size.restype = SZ
     lib.paged_prefill_nvfp4.argtypes = [C, P, P, P, P, I32, I32, I32, I32, I32, I32, F, I32, P, I32,
@@ -106,9 +108,16 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be a {dtype} CUDA tensor")
 
 
+_IN_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+_OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
+
+
 def append(cache: NVFP4KVCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor):
-    """nvfp4_kv_append: k, v bf16 [T][Hkv][128] (head/dim contiguous); slot_mapping int64 [T]."""
-    _need(k, torch.bfloat16, "k"); _need(v, torch.bfloat16, "v")
+    """nvfp4_kv_append: k, v bf16 or fp16 [T][Hkv][128] (head/dim contiguous, same dtype);
+    slot_mapping int64 [T]."""
+    if k.dtype not in _IN_DTYPES or v.dtype != k.dtype:
+        raise TypeError(f"k and v must both be bfloat16 or both float16, got {k.dtype}, {v.dtype}")
+    _need(k, k.dtype, "k"); _need(v, k.dtype, "v")
     _need(slot_mapping, torch.int64, "slot_mapping")
     if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (cache.num_kv_heads, HEAD_DIM):
         raise ValueError(f"k/v must be [T][{cache.num_kv_heads}][{HEAD_DIM}]")
@@ -118,8 +127,26 @@ def append(cache: NVFP4KVCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: 
         raise ValueError("slot_mapping must be contiguous with one slot per token")
     d = cache.desc()
     _check(load_library().nvfp4_kv_append(ctypes.byref(d), k.data_ptr(), v.data_ptr(), k.stride(0),
-                                          v.stride(0), slot_mapping.data_ptr(), k.shape[0],
-                                          _stream()))
+                                          v.stride(0), _IN_DTYPES[k.dtype], slot_mapping.data_ptr(),
+                                          k.shape[0], _stream()))
+
+
+def dequant(cache: NVFP4KVCache, slot_mapping: torch.Tensor, out_dtype=torch.bfloat16):
+    """nvfp4_kv_dequant: the cache rows of the given slots (int64 [T]; slot < 0 -> zero row) as
+    (k, v), each [T][Hkv][128] of out_dtype (bfloat16, float16 or float32)."""
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out_dtype must be bfloat16, float16 or float32, got {out_dtype}")
+    if not slot_mapping.is_contiguous() or slot_mapping.dim() != 1:
+        raise ValueError("slot_mapping must be a contiguous 1-D tensor")
+    t = slot_mapping.shape[0]
+    k = torch.empty((t, cache.num_kv_heads, HEAD_DIM), dtype=out_dtype, device=slot_mapping.device)
+    v = torch.empty_like(k)
+    d = cache.desc()
+    _check(load_library().nvfp4_kv_dequant(ctypes.byref(d), slot_mapping.data_ptr(), t,
+                                           k.data_ptr(), v.data_ptr(), _OUT_DTYPES[out_dtype],
+                                           _stream()))
+    return k, v
 
 
 def prefill_workspace_size(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,

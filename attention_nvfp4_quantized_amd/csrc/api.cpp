@@ -111,9 +111,11 @@ const char* nvfp4kv_last_error(void) { return g_last_error.c_str(); }
 int32_t nvfp4kv_version(void) { return 100; }
 
 int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
-                    int64_t k_token_stride, int64_t v_token_stride, const int64_t* slot_mapping,
-                    int32_t num_tokens, void* stream) {
+                    int64_t k_token_stride, int64_t v_token_stride, int32_t input_dtype,
+                    const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
   if (int e = check_cache(cache)) return e;
+  if (input_dtype != NVFP4KV_IN_BF16 && input_dtype != NVFP4KV_IN_F16)
+    return fail(NVFP4KV_EINVAL, "input_dtype %d unknown", input_dtype);
   if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "num_tokens < 0");
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping) return fail(NVFP4KV_EINVAL, "k, v or slot_mapping is NULL");
@@ -136,7 +138,34 @@ int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
   p.v_global = cache->v_global;
   p.num_tokens = num_tokens;
   p.num_kv_heads = cache->num_kv_heads;
+  p.fp16_in = input_dtype == NVFP4KV_IN_F16;
   return check_launch(nvfp4kv::launch_append(p, (hipStream_t)stream), "append launch");
+}
+
+int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
+                     int32_t num_tokens, void* k_out, void* v_out, int32_t out_dtype,
+                     void* stream) {
+  if (int e = check_cache(cache)) return e;
+  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32 && out_dtype != NVFP4KV_OUT_F16)
+    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
+  if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "num_tokens < 0");
+  if (num_tokens == 0) return ok();
+  if (!slot_mapping || !k_out || !v_out) return fail(NVFP4KV_EINVAL, "slot_mapping, k_out or v_out is NULL");
+  if (!aligned16(k_out) || !aligned16(v_out)) return fail(NVFP4KV_EINVAL, "k_out / v_out must be 16-byte aligned");
+  nvfp4kv::DequantParams p{};
+  p.slots = slot_mapping;
+  p.k_data = cache->k_data;
+  p.k_scale = cache->k_scale;
+  p.v_data = cache->v_data;
+  p.v_scale = cache->v_scale;
+  p.k_global = cache->k_global;
+  p.v_global = cache->v_global;
+  p.k_out = k_out;
+  p.v_out = v_out;
+  p.out_dtype = out_dtype;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = cache->num_kv_heads;
+  return check_launch(nvfp4kv::launch_dequant(p, (hipStream_t)stream), "dequant launch");
 }
 
 size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,

@@ -42,15 +42,21 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne(float q) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// Quantize one 16-value block held as 8 bf16 pairs: returns the E4M3 scale code and the
-// packed codes (element 2i in the low nibble of byte i).
-template <bool UNIT_G>
+// Quantize one 16-value block held as 8 pairs of bf16 (or fp16) values: returns the E4M3
+// scale code and the packed codes (element 2i in the low nibble of byte i).
+template <bool UNIT_G, bool FP16_IN>
 __device__ __forceinline__ uint32_t quantize_block(const uint32_t (&w)[8], float g, u32x2& packed) {
   float y[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    y[2 * i] = __uint_as_float(w[i] << 16);
-    y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    if (FP16_IN) {  // every binary16 value converts exactly
+      const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+      y[2 * i] = (float)h[0];
+      y[2 * i + 1] = (float)h[1];
+    } else {
+      y[2 * i] = __uint_as_float(w[i] << 16);
+      y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
   }
   if (!UNIT_G) {
 #pragma unroll
@@ -84,7 +90,7 @@ __device__ __forceinline__ uint32_t quantize_block(const uint32_t (&w)[8], float
 }
 
 // Grid: x = groups of 64 tokens (4 wavefronts x 16), y = KV head * 2 + (0 for K, 1 for V).
-template <bool UNIT_G>
+template <bool UNIT_G, bool FP16_IN>
 __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
   const int which = blockIdx.y & 1;
   const int h = blockIdx.y >> 1;
@@ -105,8 +111,8 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
   const uint32_t wa[8] = {in0[0], in0[1], in0[2], in0[3], in1[0], in1[1], in1[2], in1[3]};
   const uint32_t wb[8] = {in2[0], in2[1], in2[2], in2[3], in3[0], in3[1], in3[2], in3[3]};
   u32x2 pa, pb;
-  const uint32_t sa = quantize_block<UNIT_G>(wa, g, pa);
-  const uint32_t sb = quantize_block<UNIT_G>(wb, g, pb);
+  const uint32_t sa = quantize_block<UNIT_G, FP16_IN>(wa, g, pa);
+  const uint32_t sb = quantize_block<UNIT_G, FP16_IN>(wb, g, pb);
 
   const int64_t page = slot >> 4;
   const int64_t row = (page * p.num_kv_heads + h) * kPageSize + (slot & 15);
@@ -118,10 +124,14 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.num_tokens + 63) / 64), (unsigned)(2 * p.num_kv_heads));
-  if (p.k_global == 1.0f && p.v_global == 1.0f)
-    hipLaunchKernelGGL(nvfp4_append_kernel<true>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(nvfp4_append_kernel<false>, grid, dim3(256), 0, stream, p);
+  const bool unit = p.k_global == 1.0f && p.v_global == 1.0f;
+  if (p.fp16_in) {
+    if (unit) hipLaunchKernelGGL((nvfp4_append_kernel<true, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((nvfp4_append_kernel<false, true>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (unit) hipLaunchKernelGGL((nvfp4_append_kernel<true, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((nvfp4_append_kernel<false, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

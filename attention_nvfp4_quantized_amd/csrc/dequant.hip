@@ -1,0 +1,80 @@
+// Standalone dequantization of NVFP4 cache rows for gfx950 ("NVFP4 KV cache A4Q prefill
+// explained", section "Preserve the capacity and decode case": quantization and dequantization
+// utilities over the linear block-scale layout).
+//
+// Grid: x = groups of 64 tokens (4 wavefronts x 16), y = KV head * 2 + (0 for K, 1 for V); lane l
+// of a wavefront converts the 32 values (16 packed bytes, two scale bytes) of quarter l%4 of
+// token l/4.  Each value is s * e2m1(code), exact in float32 (the fp4 conversion is exact and
+// the E4M3 scale is applied by one exact multiply), times g (one float32 rounding), then rounded
+// to nearest-even in the output type.  Slots < 0 give zero rows.
+#include "device_common.hpp"
+#include "kernel_params.hpp"
+
+namespace nvfp4kv {
+
+template <int OUT>  // 0 bf16, 1 f32, 2 f16
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(DequantParams p) {
+  const int which = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane >> 2);
+  const int qq = lane & 3;
+  if (t >= p.num_tokens) return;
+  const int64_t slot = p.slots[t];
+  float x[32];
+  if (slot >= 0) {
+    const int64_t row = ((slot >> 4) * p.num_kv_heads + h) * kPageSize + (slot & 15);
+    const u32x4 d = *(const u32x4*)((which == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq);
+    const uint32_t sw = *(const uint16_t*)((which == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq);
+    const float g = which == 0 ? p.k_global : p.v_global;
+    const float s0 = e4m3_byte<0>(sw), s1 = e4m3_byte<1>(sw);
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const float s = wd < 2 ? s0 : s1;
+      const f32x2 a = e2m1_pair<0>(d[wd]), b = e2m1_pair<1>(d[wd]);
+      const f32x2 c = e2m1_pair<2>(d[wd]), e = e2m1_pair<3>(d[wd]);
+      const float v8[8] = {a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[8 * wd + i] = (v8[i] * s) * g;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+  }
+  const int64_t off = ((int64_t)t * p.num_kv_heads + h) * kHeadDim + 32 * qq;
+  void* out = which == 0 ? p.k_out : p.v_out;
+  if (OUT == 1) {
+    float* o = (float*)out + off;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(f32x4*)(o + 4 * i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+  } else {
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (OUT == 0) {
+        w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      } else {
+        f16x2 hv;
+        hv[0] = (_Float16)x[2 * i];
+        hv[1] = (_Float16)x[2 * i + 1];
+        w[i] = __builtin_bit_cast(uint32_t, hv);
+      }
+    }
+    uint16_t* o = (uint16_t*)out + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(o + 8 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+  }
+}
+
+hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.num_tokens + 63) / 64), (unsigned)(2 * p.num_kv_heads));
+  switch (p.out_dtype) {
+    case 0: hipLaunchKernelGGL(nvfp4_dequant_kernel<0>, grid, dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(nvfp4_dequant_kernel<1>, grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(nvfp4_dequant_kernel<2>, grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

@@ -20,6 +20,22 @@ struct AppendParams {
   float v_global;
   int32_t num_tokens;
   int32_t num_kv_heads;
+  int32_t fp16_in;  // input is IEEE binary16 (else bf16)
+};
+
+struct DequantParams {
+  const int64_t* slots;
+  const uint8_t* k_data;
+  const uint8_t* k_scale;
+  const uint8_t* v_data;
+  const uint8_t* v_scale;
+  float k_global;
+  float v_global;
+  void* k_out;
+  void* v_out;
+  int32_t out_dtype;  // 0 bf16, 1 f32, 2 f16
+  int32_t num_tokens;
+  int32_t num_kv_heads;
 };
 
 struct PrefillParams {
@@ -83,6 +99,7 @@ struct DecodeParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

@@ -55,6 +55,10 @@ extern "C" {
 
 #define NVFP4KV_OUT_BF16 0
 #define NVFP4KV_OUT_F32 1
+#define NVFP4KV_OUT_F16 2 /* nvfp4_kv_dequant only */
+
+#define NVFP4KV_IN_BF16 0 /* writer input types of nvfp4_kv_append */
+#define NVFP4KV_IN_F16 1
 
 typedef struct nvfp4kv_cache {
   uint8_t* k_data;  /* [num_pages][num_kv_heads][page_size][head_dim/2]  */
@@ -72,17 +76,35 @@ typedef struct nvfp4kv_cache {
 
 /*
  * Cache append ([B] "NVFP4 stores 4.5 bits per value before padding", "Decode can win on fewer
- * bytes read"; [C] "The cache quantizes values during serving"): quantize bf16 K and V, choose
- * the block scales, pack, and write each token's row to its slot.
- *   k, v          bf16 [num_tokens][num_kv_heads][head_dim]; heads and dims contiguous, tokens
- *                 `k_token_stride` / `v_token_stride` elements apart (>= num_kv_heads*head_dim).
+ * bytes read"; [C] "The cache quantizes values during serving"; [A] "Preserve the capacity and
+ * decode case": the writer quantizes BF16 or FP16 input): quantize K and V, choose the block
+ * scales, pack, and write each token's row to its slot.
+ *   k, v          [num_tokens][num_kv_heads][head_dim] of `input_dtype` (NVFP4KV_IN_BF16 or
+ *                 NVFP4KV_IN_F16); heads and dims contiguous, tokens `k_token_stride` /
+ *                 `v_token_stride` elements apart (>= num_kv_heads*head_dim, multiples of 8,
+ *                 16-byte aligned base pointers).
  *   slot_mapping  int64 [num_tokens]; slot < 0 skips the token; slots must be distinct and
  *                 < num_pages * page_size.
  * Bytes written are bit-identical to the format definition above.  num_tokens == 0 is a no-op.
  */
 int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
-                    int64_t k_token_stride, int64_t v_token_stride, const int64_t* slot_mapping,
-                    int32_t num_tokens, void* stream);
+                    int64_t k_token_stride, int64_t v_token_stride, int32_t input_dtype,
+                    const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * Standalone dequantization ([A] "Preserve the capacity and decode case": quantization and
+ * dequantization utilities over the linear block-scale layout): the cache rows of the given
+ * slots as values g * s * e2m1(code).  s * e2m1 is exact in float32; the product with g is one
+ * float32 rounding, and the result is rounded to nearest-even in the output type (with g = 1
+ * every value is exact in bf16 and fp16).
+ *   slot_mapping  int64 [num_tokens]; slot < 0 gives a zero row.
+ *   k_out, v_out  [num_tokens][num_kv_heads][head_dim], contiguous, of `out_dtype`
+ *                 (NVFP4KV_OUT_BF16, NVFP4KV_OUT_F16 or NVFP4KV_OUT_F32), 16-byte aligned.
+ * num_tokens == 0 is a no-op.
+ */
+int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
+                     int32_t num_tokens, void* k_out, void* v_out, int32_t out_dtype,
+                     void* stream);
 
 /*
  * Causal paged prefill over the NVFP4 cache with bf16 queries ([A] "Why NVFP4 KV cache A4Q

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for n in ("nvfp4_kv_append", "paged_prefill_nvfp4", "paged_decode_nvfp4",
+    for n in ("nvfp4_kv_append", "nvfp4_kv_dequant", "paged_prefill_nvfp4", "paged_decode_nvfp4",
               "paged_prefill_nvfp4_workspace_size", "paged_decode_nvfp4_workspace_size",
               "nvfp4kv_last_error", "nvfp4kv_version"):
         assert n in names, names
@@ -56,17 +56,34 @@ def _err():
 def test_append_rejects_bad_cache(over, code, needle):
     lib = load_library()
     d = _desc(**over)
-    rc = lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 16, 4, None)
+    rc = lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 0, 16, 4, None)
     assert rc == code and needle in _err()
 
 
 def test_append_rejects_short_stride_and_null_inputs():
     lib = load_library()
     d = _desc()
-    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 512, 1024, 16, 4, None) == -1
-    assert lib.nvfp4_kv_append(ctypes.byref(d), None, 16, 1024, 1024, 16, 4, None) == -1
-    assert lib.nvfp4_kv_append(None, 16, 16, 1024, 1024, 16, 4, None) == -1
-    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 16, 0, None) == 0
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 512, 1024, 0, 16, 4, None) == -1
+    assert lib.nvfp4_kv_append(ctypes.byref(d), None, 16, 1024, 1024, 0, 16, 4, None) == -1
+    assert lib.nvfp4_kv_append(None, 16, 16, 1024, 1024, 0, 16, 4, None) == -1
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 0, 16, 0, None) == 0
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 1, 16, 0, None) == 0
+    assert _err() == ""
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 2, 16, 4, None) == -1
+    assert b"input_dtype" in lib.nvfp4kv_last_error()
+
+
+def test_dequant_argument_checks():
+    lib = A.load_library()
+    d = _desc()
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), 16, 4, 16, 16, 3, None) == -1
+    assert b"out_dtype" in lib.nvfp4kv_last_error()
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), None, 4, 16, 16, 0, None) == -1
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), 16, 4, 8, 16, 0, None) == -1
+    assert b"aligned" in lib.nvfp4kv_last_error()
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), 16, -1, 16, 16, 0, None) == -1
+    assert lib.nvfp4_kv_dequant(None, 16, 4, 16, 16, 0, None) == -1
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), 16, 0, 16, 16, 2, None) == 0
     assert _err() == ""
 
 

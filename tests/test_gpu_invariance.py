@@ -8,7 +8,7 @@ import workload as W
 from oracle import attention as oattn
 from oracle import cache as ocache
 from oracle import codec as ocodec
-from gpu_cases import (LSE_ATOL, GpuPrefillCase, assert_attention_close, assert_cache_equal, dev, dev_bf16,
+from gpu_cases import (DEV, LSE_ATOL, GpuPrefillCase, assert_attention_close, assert_cache_equal, dev, dev_bf16,
                        oracle_cache, oracle_prefill, say)
 
 pytestmark = pytest.mark.gpu
@@ -19,22 +19,21 @@ def _case(q_lens, kv_lens, hq=32, hkv=8, seed=3001, k_out=0, **kw):
     return W.prefill_case(w)
 
 
-def test_codec_exhaustive_through_append():
-    say("[codec] every finite bf16 value under every E4M3 scale, and every bf16 amax")
-    vals = W.bf16_bits_to_f32(np.arange(65536, dtype=np.uint16))
-    finite = np.isfinite(vals)
+def _exhaustive_blocks(values: np.ndarray) -> np.ndarray:
+    """Blocks holding every finite value under every nonzero E4M3 scale (amax = 6 s places the
+    scale exactly), every positive amax, and the special cases."""
     blocks = []
     for c in range(1, 127):
         s = float(ocodec.e4m3_value(c))
         amax = np.float32(6.0 * s)
-        pool = vals[finite & (np.abs(vals) <= amax)]
+        pool = values[np.abs(values) <= amax]
         n = (len(pool) + 14) // 15
         blk = np.zeros((n, 16), np.float32)
         flat = np.zeros(n * 15, np.float32); flat[: len(pool)] = pool
         blk[:, 1:] = flat.reshape(n, 15)
         blk[:, 0] = amax
         blocks.append(blk)
-    amaxes = vals[finite & (vals > 0)]
+    amaxes = values[values > 0]
     one = np.zeros((len(amaxes), 16), np.float32); one[:, 7] = amaxes; one[:, 8] = -amaxes / 3
     blocks.append(one)
     special = np.zeros((4, 16), np.float32)
@@ -44,19 +43,57 @@ def test_codec_exhaustive_through_append():
     blocks.append(special)
     x = np.concatenate(blocks)
     pad = (-len(x)) % 8
-    x = np.concatenate([x, np.zeros((pad, 16), np.float32)])
-    bits = W.f32_to_bf16_bits(x).reshape(-1, 1, 128)  # exact: every value is bf16
+    return np.concatenate([x, np.zeros((pad, 16), np.float32)])
+
+
+@pytest.mark.parametrize("input_dtype", ["bf16", "fp16"])
+def test_codec_exhaustive_through_append(input_dtype):
+    say(f"[codec] every finite {input_dtype} value under every E4M3 scale, and every {input_dtype} amax")
+    if input_dtype == "bf16":
+        vals = W.bf16_bits_to_f32(np.arange(65536, dtype=np.uint16))
+    else:
+        vals = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float32)
+    x = _exhaustive_blocks(vals[np.isfinite(vals)])
+    if input_dtype == "bf16":
+        bits = W.f32_to_bf16_bits(x).reshape(-1, 1, 128)  # both sides read these bit patterns
+        to_dev = dev_bf16
+    else:
+        bits = x.astype(np.float16).view(np.uint16).reshape(-1, 1, 128)  # both sides read these bit patterns
+        to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(DEV).view(torch.float16)
     t = bits.shape[0]
     pages = (t + 15) // 16
     slots = np.random.default_rng(0).permutation(pages * 16)[:t].astype(np.int64)
     cache = A.NVFP4KVCache(pages, 1)
-    A.append(cache, dev_bf16(bits), dev_bf16(bits[::-1].copy()), dev(slots))
+    A.append(cache, to_dev(bits), to_dev(bits[::-1].copy()), dev(slots))
     torch.cuda.synchronize()
     oc = ocache.PagedCache(pages, 1)
-    oc.append(bits, bits[::-1].copy(), slots)
+    oc.append(bits, bits[::-1].copy(), slots, input_dtype=input_dtype)
     got = [t_.cpu().numpy() for t_ in (cache.k_data, cache.k_scale, cache.v_data, cache.v_scale)]
     say(f"  {x.size} values in {t} tokens")
     assert_cache_equal(got, oc)
+
+
+@pytest.mark.parametrize("gk,gv", [(1.0, 1.0), (1.5, 0.75)])
+def test_dequant_bit_exact(gk, gv):
+    say(f"[dequant] bf16 / fp16 / f32 rows of random slots, k_global {gk}, v_global {gv}")
+    pc = _case([70, 41], [70, 41], 8, 4, 3010, k_out=4)
+    g = GpuPrefillCase(pc, k_global=gk, v_global=gv)
+    g.append()
+    oc = oracle_cache(pc, k_global=gk, v_global=gv)
+    rng = np.random.default_rng(3)
+    slots = rng.permutation(pc.slot_mapping)[:97].copy()
+    slots[[0, 50, 96]] = -1
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16), ("f32", torch.float32)):
+        k, v = A.dequant(g.cache, dev(slots), out_dtype=dt)
+        torch.cuda.synchronize()
+        ok, ov = oc.dequant_slots(slots, name)
+        for got, exp, what in ((k, ok, "k"), (v, ov, "v")):
+            gh = got.cpu().view(torch.int16).numpy().view(np.uint16) if name != "f32" else got.cpu().numpy()
+            if name == "f32":
+                assert np.array_equal(gh.view(np.uint32), np.asarray(exp, np.float32).view(np.uint32)), (name, what)
+            else:
+                bad = np.argwhere(gh != exp)
+                assert len(bad) == 0, f"{name} {what}: {len(bad)} differ, first {bad[0].tolist()}"
 
 
 def test_append_global_scales_and_skipped_slots():
