@@ -190,6 +190,37 @@ def run_decode(args, torch, A):
     }
 
 
+def run_full_prefill(name, torch, A, reps=8, warmup=4):
+    """Kernel time of the append and the causal prefill of a full-length single request (the
+    pages' benchmark matrix asks for full 8K and 32K prefill next to the tail shapes)."""
+    w = W.get(name)
+    pc = W.prefill_case(w)
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    k, v = bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch)
+    slots = torch.from_numpy(pc.slot_mapping).cuda()
+    q = bf16_dev(pc.q_bits, torch)
+    cu = torch.from_numpy(pc.cu_seqlens_q).cuda()
+    kv = torch.from_numpy(pc.kv_lens).cuda()
+    bt = torch.from_numpy(pc.layout.block_table).cuda()
+    out = torch.empty((pc.total_q, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for i in range(warmup + reps):
+        e = ev[i - warmup] if i >= warmup else None
+        if e: e[0].record()
+        A.append(cache, k, v, slots)
+        if e: e[1].record()
+        A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out)
+        if e: e[2].record()
+    torch.cuda.synchronize()
+    pre = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    app = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
+    return {"workload": name, "q_len": int(w.q_lens[0]), "kv_len": int(w.kv_lens[0]),
+            "prefill_ms": round(pre, 4), "TFLOPs": round(flops / (pre * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (pre * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "append_us": round(app * 1e3, 2), "flop_per_call": flops}
+
+
 def run_short_prefill(name, torch, A, reps=20, warmup=5):
     """Prefill-only timing of a short-query workload (tail128: 4 x 128 queries over 2,048 keys;
     tail16: 8 x 16 queries over 16,384 keys): median µs per call with a 512 MB buffer written
@@ -286,6 +317,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-short", action="store_true", help="skip the tail128 / tail16 prefill timings")
+    ap.add_argument("--no-matrix", action="store_true", help="skip the full 8K / 32K prefill timings")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -324,6 +356,8 @@ def main():
         line["decode"] = run_decode(args, torch, A)
     if not args.no_short:
         line["short_prefill"] = [run_short_prefill(n, torch, A) for n in ("tail128", "tail16")]
+    if not args.no_matrix:
+        line["prefill_matrix"] = [run_full_prefill(n, torch, A) for n in ("full8k", "full32k")]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(pre["pc"])
     print(json.dumps(line))

@@ -66,17 +66,26 @@ def test_prefill_parity_all_rows(name):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
-def test_prefill_parity_full16k_sampled_rows():
-    w = W.get("full16k")
-    say("[prefill] full16k sampled rows")
+def _full_rows(n):
+    """Sampled rows of an n-token full prefill: the first tiles, tile and page edges, the middle
+    and the last rows."""
+    r = FULL16K_ROWS[FULL16K_ROWS < n // 2]
+    return np.unique(np.concatenate([r, [n // 2 - 1, n // 2, n - 65, n - 64, n - 2, n - 1]]))
+
+
+@pytest.mark.parametrize("name", ["full8k", "full16k", "full32k"])
+def test_prefill_parity_full_sampled_rows(name):
+    w = W.get(name)
+    say(f"[prefill] {name} sampled rows")
     pc = W.prefill_case(w)
     g = GpuPrefillCase(pc)
     g.append()
     o32 = g.prefill(torch.float32).cpu().numpy()
     o16 = g.prefill(torch.bfloat16).float().cpu().numpy()
-    ref, _ = oracle_prefill(pc, oracle_cache(pc), rows=FULL16K_ROWS)
-    assert_attention_close(o32, ref, "full16k fp32")
-    assert_attention_close_bf16(o16, ref, "full16k bf16")
+    rows = FULL16K_ROWS if name == "full16k" else _full_rows(w.kv_lens[0])
+    ref, _ = oracle_prefill(pc, oracle_cache(pc), rows=rows)
+    assert_attention_close(o32, ref, f"{name} fp32")
+    assert_attention_close_bf16(o16, ref, f"{name} bf16")
 
 
 def test_prefill_parity_tail16_sampled_sequences():

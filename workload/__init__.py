@@ -139,6 +139,8 @@ def get(name_or_index) -> Workload:
         "full16k": lambda: Workload("full16k", 3, 1, [16384], [16384], 32, 8, 20),
         "tail16": lambda: Workload("tail16", 4, 8, [16] * 8, [16384] * 8, 32, 8, 0),
         "decode": lambda: _decode_workload(),
+        "full8k": lambda: Workload("full8k", 6, 1, [8192], [8192], 32, 8, 20),
+        "full32k": lambda: Workload("full32k", 7, 1, [32768], [32768], 32, 8, 20),
     }
     if isinstance(name_or_index, int):
         name_or_index = list(table)[name_or_index - 1]
@@ -151,7 +153,7 @@ def _decode_workload(batch: int = 64, steps: int = 64, kv_min: int = 16384,
     return Workload("decode", 5, batch, [1] * batch, lens, 32, 8, 0, decode_steps=steps)
 
 
-ALL = ("tiny", "tail128", "full16k", "tail16", "decode")
+ALL = ("tiny", "tail128", "full16k", "tail16", "decode", "full8k", "full32k")
 
 
 def custom(name: str, q_lens, kv_lens, num_qo_heads: int, num_kv_heads: int, seed: int,
