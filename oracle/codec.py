@@ -121,6 +121,30 @@ def quantize(x: np.ndarray, g: float = 1.0):
     return codes, sc
 
 
+# ---- FP8 (E4M3FN) KV cache, the control format --------------------------------------------
+# Every value is one E4M3FN byte under a per-tensor scale g: the writer stores
+# E4M3_RNE_sat(fl32(x / g)) with the sign bit copied from y, the reader multiplies by g.  (The
+# pages compare NVFP4 against an FP8 cache throughout; its exact layout is a reading.)
+
+def e4m3_encode_signed(y) -> np.ndarray:
+    """E4M3FN code of float values: sign bit 7 copied from y, magnitude rounded to nearest with
+    ties to the even code, saturating at 448 (0x7E)."""
+    y = np.asarray(y, dtype=np.float64)
+    return ((np.signbit(y).astype(np.uint8) << 7) | e4m3_encode(np.abs(y))).astype(np.uint8)
+
+
+def quantize_fp8(x: np.ndarray, g: float = 1.0) -> np.ndarray:
+    """FP8 cache codes of float32 values: E4M3FN of y = fl32(x / g)."""
+    x = np.asarray(x, dtype=np.float32)
+    y = (x / np.float32(g)).astype(np.float32)
+    return e4m3_encode_signed(y.astype(np.float64))
+
+
+def dequantize_fp8(codes: np.ndarray, g: float = 1.0) -> np.ndarray:
+    """Read-side value of FP8 cache codes: g * e4m3(code), in float64."""
+    return float(g) * e4m3_value(np.asarray(codes, dtype=np.uint8))
+
+
 def pack(codes: np.ndarray) -> np.ndarray:
     """Two E2M1 codes per byte: element 2i in the low nibble, 2i+1 in the high nibble."""
     codes = np.asarray(codes, dtype=np.uint8)

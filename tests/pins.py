@@ -106,8 +106,12 @@ def _fraction_e4m3_table():
 
 def expected_scale_code(amax: Fraction, table=None) -> int:
     """Exact E4M3 rounding (nearest, ties to even code, saturating) of amax/6."""
+    return expected_e4m3_code(amax / 6, table)
+
+
+def expected_e4m3_code(q: Fraction, table=None) -> int:
+    """Exact E4M3 rounding (nearest, ties to even code, saturating) of q >= 0."""
     table = table or _fraction_e4m3_table()
-    q = amax / 6
     if q >= table[-1]:
         return 126
     i = bisect.bisect_left(table, q)
@@ -233,6 +237,20 @@ def check_dequant_routes_agree(codec, cache_mod, seed=5):
             assert not np.any(np.asarray(got[-1], np.float64)), out
 
 
+def check_fp8_encode_exhaustive(codec):
+    """FP8 cache encoding of every finite bf16 and fp16 value (both signs) against exact
+    rational nearest-even rounding onto the E4M3FN values, saturating at 448."""
+    table = _fraction_e4m3_table()
+    for vals in (bf16_value(finite_bf16_patterns()), fp16_value_by_fields(finite_fp16_patterns())):
+        got = codec.e4m3_encode_signed(np.asarray(vals, np.float64))
+        mags = np.abs(np.asarray(vals, np.float64))
+        uniq, inv = np.unique(mags, return_inverse=True)
+        exp_mag = np.array([expected_e4m3_code(Fraction(float(a)), table) for a in uniq], np.uint8)[inv]
+        exp = (np.signbit(vals).astype(np.uint8) << 7) | exp_mag
+        bad = np.nonzero(got != exp)[0]
+        assert len(bad) == 0, f"{len(bad)} mismatches, first y={vals[bad[0]]!r}"
+
+
 def check_worked_block(codec):
     g = golden("worked_block.json")
     x = np.array(g["values"], np.float32)
@@ -298,8 +316,17 @@ def brute_force_attention(q, k, v, last_visible, sm_scale):
     return np.array(out), np.array(lses)
 
 
-def check_attention_bruteforce(codec, cache_mod, attention, seed=7, head_dim=32):
-    """Tiny ragged shapes, all rows, GQA 2, vs Python loops over independently dequantized K/V."""
+def _nvfp4_round_trip(codec, x):
+    c, sc = codec.quantize(x)
+    return codec.dequantize(codec.pack(c), sc)
+
+
+def check_attention_bruteforce(codec, cache_mod, attention, seed=7, head_dim=32,
+                               make_cache=None, round_trip=None):
+    """Tiny ragged shapes, all rows, GQA 2, vs Python loops over independently dequantized K/V
+    (NVFP4 by default; `make_cache` / `round_trip` select another cache format)."""
+    make_cache = make_cache or cache_mod.PagedCache
+    round_trip = round_trip or (lambda x: _nvfp4_round_trip(codec, x))
     rng = np.random.default_rng(seed)
     q_lens, kv_lens = [1, 3, 5], [1, 7, 9]
     hq, hkv, ps = 4, 2, 16
@@ -309,7 +336,7 @@ def check_attention_bruteforce(codec, cache_mod, attention, seed=7, head_dim=32)
     off = 0
     for b, n in enumerate(pages):
         bt[b, :n] = perm[off:off + n]; off += n
-    cache = cache_mod.PagedCache(sum(pages) + 2, hkv, head_dim=head_dim, page_size=ps)
+    cache = make_cache(sum(pages) + 2, hkv, head_dim=head_dim, page_size=ps)
     sm = 1 / math.sqrt(head_dim)
     qs, ks, vs = [], [], []
     for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
@@ -327,10 +354,8 @@ def check_attention_bruteforce(codec, cache_mod, attention, seed=7, head_dim=32)
     o, lse = attention.prefill(cache, qb, cu, kv_lens, bt, sm)
     for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
         for kvh in range(hkv):
-            kc, ksc = codec.quantize(bf16_value(ks[b][:, kvh]))
-            vc, vsc = codec.quantize(bf16_value(vs[b][:, kvh]))
-            kd = codec.dequantize(codec.pack(kc), ksc)
-            vd = codec.dequantize(codec.pack(vc), vsc)
+            kd = round_trip(bf16_value(ks[b][:, kvh]))
+            vd = round_trip(bf16_value(vs[b][:, kvh]))
             for h in range(kvh * (hq // hkv), (kvh + 1) * (hq // hkv)):
                 qv = bf16_value(qs[b][:, h]).astype(np.float64)
                 ref_o, ref_l = brute_force_attention(qv, kd, vd, [kl - ql + i for i in range(ql)], sm)
