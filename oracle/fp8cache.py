@@ -41,6 +41,22 @@ class Fp8PagedCache:
             codes = codec.quantize_fp8(codec.input_to_f32(bits, input_dtype), g)
             data[page, :, off, :] = codes[keep]
 
+    def dequant_slots(self, slot_mapping: np.ndarray, out_dtype: str = "bf16"):
+        """The standalone dequantization: rows of the given slots as g * e4m3(code), formed in
+        float32 (e4m3(code) is exact there; the product with g rounds once) and rounded to
+        nearest-even in the output type; slots < 0 give zero rows.  Returns (k, v), each
+        [n][num_kv_heads][head_dim] (bit patterns for bf16 / fp16, float32 for f32)."""
+        slots = np.asarray(slot_mapping, dtype=np.int64)
+        keep = slots >= 0
+        page = np.where(keep, slots // self.page_size, 0)
+        off = np.where(keep, slots % self.page_size, 0)
+        out = []
+        for data, g in ((self.k_data, self.k_global), (self.v_data, self.v_global)):
+            x = codec.e4m3_value(data[page, :, off, :]).astype(np.float32) * np.float32(g)
+            x = np.where(keep[:, None, None], x, np.float32(0)).astype(np.float32)
+            out.append(codec.round_to_dtype(x, out_dtype))
+        return out[0], out[1]
+
     def gather(self, block_table_row: np.ndarray, n: int):
         """Dequantized K and V of positions 0..n-1 of one sequence: float64 [n][H][D]."""
         pos = np.arange(n)

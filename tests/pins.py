@@ -251,6 +251,31 @@ def check_fp8_encode_exhaustive(codec):
         assert len(bad) == 0, f"{len(bad)} mismatches, first y={vals[bad[0]]!r}"
 
 
+def check_fp8_dequant(codec, fp8_mod):
+    """FP8 standalone dequantization of every finite E4M3FN code (both signs) against exact
+    rationals: g * e4m3(code) rounded to float32, then nearest-even to the output type; g = 1 for
+    K (every product exact) and fl32(1/3) for V (the product rounds); slot < 0 gives zeros."""
+    table = _fraction_e4m3_table()
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    c = fp8_mod.Fp8PagedCache(1, 1, k_global=1.0, v_global=float(np.float32(1 / 3)))
+    c.k_data[0, 0, :2, :] = np.resize(codes, (2, 128))
+    c.v_data[0, 0, :2, :] = np.resize(codes, (2, 128))
+    value = {int(x): (-1 if x & 0x80 else 1) * table[x & 0x7F] for x in codes}
+    flat = np.resize(codes, 256)
+    for out, (emin, mant, decode) in {"bf16": (-126, 7, bf16_value), "fp16": (-14, 10, fp16_value_by_fields),
+                                      "f32": (-126, 23, None)}.items():
+        k, v = c.dequant_slots(np.array([0, 1, -1]), out)
+        for got, g in ((k, Fraction(1)), (v, Fraction(float(np.float32(1 / 3))))):
+            vals = np.asarray(got[:2, 0].reshape(-1) if decode is None else decode(got[:2, 0].reshape(-1)), np.float64)
+            for i, x in enumerate(flat):
+                f32 = nearest_even_fraction(value[int(x)] * g, -126, 23)
+                exp = nearest_even_fraction(f32, emin, mant)
+                assert Fraction(float(vals[i])) == exp, (out, int(x), float(vals[i]), float(exp))
+                if exp == 0:
+                    assert np.signbit(vals[i]) == bool(x & 0x80), (out, int(x))
+            assert not np.any(np.asarray(got[2], np.float64)), out
+
+
 def check_worked_block(codec):
     g = golden("worked_block.json")
     x = np.array(g["values"], np.float32)

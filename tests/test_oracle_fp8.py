@@ -24,6 +24,24 @@ def test_fp8_saturation_and_global_scale():
     assert np.array_equal(codec.dequantize_fp8(codec.quantize_fp8(y * 4, 4.0), 4.0), [12.0, -2.0])
 
 
+def test_fp8_dequant_exhaustive_vs_exact_rationals():
+    pins.check_fp8_dequant(codec, fp8cache)
+
+
+def test_pins_catch_fp8_dequant_without_global_scale():
+    class C(fp8cache.Fp8PagedCache):
+        def dequant_slots(self, slot_mapping, out_dtype="bf16"):
+            g = self.v_global
+            self.v_global = 1.0  # drops the per-tensor scale
+            try:
+                return super().dequant_slots(slot_mapping, out_dtype)
+            finally:
+                self.v_global = g
+    import types
+    with pytest.raises(AssertionError):
+        pins.check_fp8_dequant(codec, types.SimpleNamespace(Fp8PagedCache=C))
+
+
 def test_fp8_attention_bruteforce():
     pins.check_attention_bruteforce(
         codec, cache, attention, make_cache=fp8cache.Fp8PagedCache,
