@@ -31,7 +31,8 @@ class CacheDesc(ctypes.Structure):
                 ("v_data", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("k_global", ctypes.c_float), ("v_global", ctypes.c_float),
                 ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_format", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,26 +82,42 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+_FORMATS = {"nvfp4": 0, "fp8": 1}
+
+
 class NVFP4KVCache:
-    """Device memory of one layer's paged NVFP4 cache (allocated with torch, zero-filled)."""
+    """Device memory of one layer's paged KV cache (allocated with torch, zero-filled).
+
+    kv_format "nvfp4": packed E2M1 codes [pages][Hkv][16][64] plus E4M3 block scales
+    [pages][Hkv][16][8] per K and V.  kv_format "fp8": the FP8 (E4M3FN) control cache, one byte
+    per value [pages][Hkv][16][128] and no scale plane."""
 
     def __init__(self, num_pages: int, num_kv_heads: int, device="cuda", k_global: float = 1.0,
-                 v_global: float = 1.0):
-        shape_d = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM // 2)
-        shape_s = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM // 16)
+                 v_global: float = 1.0, kv_format: str = "nvfp4"):
+        if kv_format not in _FORMATS:
+            raise ValueError(f"kv_format must be one of {sorted(_FORMATS)}, got {kv_format!r}")
         z = lambda s: torch.zeros(s, dtype=torch.uint8, device=device)  # noqa: E731
-        self.k_data, self.k_scale = z(shape_d), z(shape_s)
-        self.v_data, self.v_scale = z(shape_d), z(shape_s)
+        if kv_format == "fp8":
+            shape_d = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM)
+            self.k_data, self.v_data = z(shape_d), z(shape_d)
+            self.k_scale = self.v_scale = None
+        else:
+            shape_d = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM // 2)
+            shape_s = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM // 16)
+            self.k_data, self.k_scale = z(shape_d), z(shape_s)
+            self.v_data, self.v_scale = z(shape_d), z(shape_s)
+        self.kv_format = kv_format
         self.num_pages, self.num_kv_heads = num_pages, num_kv_heads
         self.k_global, self.v_global = float(k_global), float(v_global)
 
     def desc(self) -> CacheDesc:
-        return CacheDesc(self.k_data.data_ptr(), self.k_scale.data_ptr(), self.v_data.data_ptr(),
-                         self.v_scale.data_ptr(), self.k_global, self.v_global, self.num_pages,
-                         PAGE_SIZE, self.num_kv_heads, HEAD_DIM)
+        return CacheDesc(self.k_data.data_ptr(), _ptr(self.k_scale), self.v_data.data_ptr(),
+                         _ptr(self.v_scale), self.k_global, self.v_global, self.num_pages,
+                         PAGE_SIZE, self.num_kv_heads, HEAD_DIM, _FORMATS[self.kv_format])
 
     def nbytes(self) -> int:
-        return sum(t.numel() for t in (self.k_data, self.k_scale, self.v_data, self.v_scale))
+        return sum(t.numel() for t in (self.k_data, self.k_scale, self.v_data, self.v_scale)
+                   if t is not None)
 
 
 def _need(t, dtype, name):

@@ -38,7 +38,10 @@ int check_launch(hipError_t e, const char* what) {
 
 int check_cache(const nvfp4kv_cache_t* c) {
   if (!c) return fail(NVFP4KV_EINVAL, "cache descriptor is NULL");
-  if (!c->k_data || !c->k_scale || !c->v_data || !c->v_scale)
+  if (c->kv_format != NVFP4KV_FORMAT_NVFP4 && c->kv_format != NVFP4KV_FORMAT_FP8)
+    return fail(NVFP4KV_EINVAL, "kv_format %d unknown", c->kv_format);
+  const bool fp8 = c->kv_format == NVFP4KV_FORMAT_FP8;
+  if (!c->k_data || !c->v_data || (!fp8 && (!c->k_scale || !c->v_scale)))
     return fail(NVFP4KV_EINVAL, "cache plane pointer is NULL");
   if (c->head_dim != 128)
     return fail(NVFP4KV_EUNSUPPORTED, "head_dim %d unsupported (K and V head size must be 128)",
@@ -139,6 +142,7 @@ int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
   p.num_tokens = num_tokens;
   p.num_kv_heads = cache->num_kv_heads;
   p.fp16_in = input_dtype == NVFP4KV_IN_F16;
+  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
   return check_launch(nvfp4kv::launch_append(p, (hipStream_t)stream), "append launch");
 }
 
@@ -165,6 +169,7 @@ int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
   p.out_dtype = out_dtype;
   p.num_tokens = num_tokens;
   p.num_kv_heads = cache->num_kv_heads;
+  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
   return check_launch(nvfp4kv::launch_dequant(p, (hipStream_t)stream), "dequant launch");
 }
 
@@ -219,6 +224,7 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
   if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
 
   nvfp4kv::PrefillParams p{};
+  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
   p.k_data = cache->k_data;
   p.k_scale = cache->k_scale;
   p.v_data = cache->v_data;
@@ -314,6 +320,7 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
   if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
 
   nvfp4kv::DecodeParams p{};
+  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
   p.k_data = cache->k_data;
   p.k_scale = cache->k_scale;
   p.v_data = cache->v_data;

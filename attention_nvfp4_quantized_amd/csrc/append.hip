@@ -122,9 +122,74 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
   *(uint16_t*)scale = (uint16_t)(sa | (sb << 8));
 }
 
+// FP8 control cache writer: each value becomes the E4M3FN byte of y = fl32(x / g), rounded to
+// nearest with ties to even, sign copied, magnitudes saturating at 448.  The input is clamped to
+// [-448, 448] first (the median keeps -0), so the hardware conversion never leaves the finite
+// range; in range it rounds to nearest-even.  Same grid and lane map as the NVFP4 writer; a lane
+// writes 32 bytes.
+template <bool UNIT_G, bool FP16_IN>
+__device__ __forceinline__ uint32_t fp8_encode4(uint32_t w0, uint32_t w1, float g) {
+  float y[4];
+  if (FP16_IN) {
+    const f16x2 a = __builtin_bit_cast(f16x2, w0), b = __builtin_bit_cast(f16x2, w1);
+    y[0] = (float)a[0]; y[1] = (float)a[1]; y[2] = (float)b[0]; y[3] = (float)b[1];
+  } else {
+    y[0] = __uint_as_float(w0 << 16); y[1] = __uint_as_float(w0 & 0xFFFF0000u);
+    y[2] = __uint_as_float(w1 << 16); y[3] = __uint_as_float(w1 & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!UNIT_G) y[i] = __fdiv_rn(y[i], g);
+    y[i] = __builtin_amdgcn_fmed3f(y[i], -448.0f, 448.0f);
+  }
+  int o = 0;
+  o = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], o, false);
+  o = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], o, true);
+  return (uint32_t)o;
+}
+
+template <bool UNIT_G, bool FP16_IN>
+__global__ __launch_bounds__(256) void fp8_append_kernel(AppendParams p) {
+  const int which = blockIdx.y & 1;
+  const int h = blockIdx.y >> 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane >> 2);
+  const int qq = lane & 3;  // values 32 qq .. 32 qq + 31
+  if (t >= p.num_tokens) return;
+  const int64_t slot = p.slots[t];
+  if (slot < 0) return;
+
+  const uint16_t* src = (which == 0 ? p.k + t * p.k_stride : p.v + t * p.v_stride) +
+                        (int64_t)h * kHeadDim + 32 * qq;
+  u32x4 in[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) in[i] = *(const u32x4*)(src + 8 * i);
+  const float g = which == 0 ? p.k_global : p.v_global;
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = fp8_encode4<UNIT_G, FP16_IN>(in[i][0], in[i][1], g);
+    o[2 * i + 1] = fp8_encode4<UNIT_G, FP16_IN>(in[i][2], in[i][3], g);
+  }
+  const int64_t row = ((slot >> 4) * p.num_kv_heads + h) * kPageSize + (slot & 15);
+  uint8_t* data = (which == 0 ? p.k_data : p.v_data) + row * kHeadDim + 32 * qq;
+  *(u32x4*)data = u32x4{o[0], o[1], o[2], o[3]};
+  *(u32x4*)(data + 16) = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.num_tokens + 63) / 64), (unsigned)(2 * p.num_kv_heads));
   const bool unit = p.k_global == 1.0f && p.v_global == 1.0f;
+  if (p.fp8) {
+    if (p.fp16_in) {
+      if (unit) hipLaunchKernelGGL((fp8_append_kernel<true, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((fp8_append_kernel<false, true>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (unit) hipLaunchKernelGGL((fp8_append_kernel<true, false>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((fp8_append_kernel<false, false>), grid, dim3(256), 0, stream, p);
+    }
+    return hipGetLastError();
+  }
   if (p.fp16_in) {
     if (unit) hipLaunchKernelGGL((nvfp4_append_kernel<true, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((nvfp4_append_kernel<false, true>), grid, dim3(256), 0, stream, p);

@@ -30,10 +30,24 @@ constexpr int kDecStep = 32;
 constexpr int kDecVStride = 288;  // bytes per staged V row (256 + 32 pad for transposed reads)
 constexpr int kDecStageBytes = kDecStep * kDecVStride;
 
+constexpr int kFmtNvfp4 = 0;  // packed E2M1 + E4M3 block scales
+constexpr int kFmtFp8 = 1;    // E4M3FN control cache: one byte per value, per-tensor scale only
+
+// One lane's share of a 32-token step: 32 head-dim values of one token in each of two 16-token
+// groups, for K and V (NVFP4: 16 packed bytes plus the dword holding two scale bytes; FP8: 32
+// bytes).
+template <int FMT>
 struct DecodeRegs {
   u32x4 kd[2], vd[2];
-  uint32_t ks[2], vs[2];
+  u32x4 kd2[FMT == kFmtFp8 ? 2 : 1], vd2[FMT == kFmtFp8 ? 2 : 1];
+  uint32_t ks[FMT == kFmtNvfp4 ? 2 : 1], vs[FMT == kFmtNvfp4 ? 2 : 1];
 };
+
+// Four E4M3FN bytes -> four fp16 values (two words), exact.
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t out[2]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
 
 // Page id of the wave-relative page index `pi` (uniform, < 128) from the two page-id registers.
 __device__ __forceinline__ int page_at(int pt0, int pt1, int pi) {
@@ -44,8 +58,9 @@ __device__ __forceinline__ int page_at(int pt0, int pt1, int pi) {
 // are unconditional: a group past the wave's range re-reads the range's last group (an L2 hit),
 // and tokens past the range are zeroed at use time, so every step issues the same 8 loads and
 // the wait counts stay exact.
+template <int FMT>
 __device__ __forceinline__ void decode_load(const DecodeParams& p, int hk, int wk0, int wk1,
-                                            int pt0, int pt1, int k, int lane, DecodeRegs& r) {
+                                            int pt0, int pt1, int k, int lane, DecodeRegs<FMT>& r) {
   const int last_group = (wk1 - 1) & ~15;
   const int q4 = lane >> 4;
 #pragma unroll
@@ -53,11 +68,20 @@ __device__ __forceinline__ void decode_load(const DecodeParams& p, int hk, int w
     const int first = min(k + 16 * g, last_group);
     const int page = page_at(pt0, pt1, (first - wk0) >> 4);
     const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (lane & 15);
-    r.kd[g] = *(const u32x4*)(p.k_data + row * kRowBytes + 16 * q4);
-    r.vd[g] = *(const u32x4*)(p.v_data + row * kRowBytes + 16 * q4);
-    // the dword holding this lane's two scale bytes (shifted into place at use time)
-    r.ks[g] = *(const uint32_t*)(p.k_scale + row * kScaleBytes + 4 * (q4 >> 1));
-    r.vs[g] = *(const uint32_t*)(p.v_scale + row * kScaleBytes + 4 * (q4 >> 1));
+    if constexpr (FMT == kFmtNvfp4) {
+      r.kd[g] = *(const u32x4*)(p.k_data + row * kRowBytes + 16 * q4);
+      r.vd[g] = *(const u32x4*)(p.v_data + row * kRowBytes + 16 * q4);
+      // the dword holding this lane's two scale bytes (shifted into place at use time)
+      r.ks[g] = *(const uint32_t*)(p.k_scale + row * kScaleBytes + 4 * (q4 >> 1));
+      r.vs[g] = *(const uint32_t*)(p.v_scale + row * kScaleBytes + 4 * (q4 >> 1));
+    } else {
+      const uint8_t* kp = p.k_data + row * kHeadDim + 32 * q4;
+      const uint8_t* vp = p.v_data + row * kHeadDim + 32 * q4;
+      r.kd[g] = *(const u32x4*)kp;
+      r.kd2[g] = *(const u32x4*)(kp + 16);
+      r.vd[g] = *(const u32x4*)vp;
+      r.vd2[g] = *(const u32x4*)(vp + 16);
+    }
   }
 }
 
@@ -68,7 +92,8 @@ struct DecodeState {
 };
 
 // One 32-token step: scores, V staging, online softmax, PV.
-__device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1, int lane,
+template <int FMT>
+__device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int wk1, int lane,
                                             const f16x8 (&qf)[4], float cs, char* stage,
                                             DecodeState& st) {
   const int q4 = lane >> 4;
@@ -77,31 +102,51 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const bool ok = k + 16 * g + t16 < wk1;  // this lane's token is in range
-    const uint32_t ksw = ok ? r.ks[g] >> (16 * (q4 & 1)) : 0u;
-    const f16x2 sc2 = e4m3_pair_h<false>(ksw);
-    const f16x2 s0 = __builtin_shufflevector(sc2, sc2, 0, 0);
-    const f16x2 s1 = __builtin_shufflevector(sc2, sc2, 1, 1);
     f32x4 a = f32x4{};
+    if constexpr (FMT == kFmtNvfp4) {
+      const uint32_t ksw = ok ? r.ks[g] >> (16 * (q4 & 1)) : 0u;
+      const f16x2 sc2 = e4m3_pair_h<false>(ksw);
+      const f16x2 s0 = __builtin_shufflevector(sc2, sc2, 0, 0);
+      const f16x2 s1 = __builtin_shufflevector(sc2, sc2, 1, 1);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint32_t o4[4];
-      dequant8_h(r.kd[g][kk], kk < 2 ? s0 : s1, o4);
-      a = mfma16h(__builtin_bit_cast(f16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t o4[4];
+        dequant8_h(r.kd[g][kk], kk < 2 ? s0 : s1, o4);
+        a = mfma16h(__builtin_bit_cast(f16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t w0 = ok ? (kk < 2 ? r.kd[g][2 * kk] : r.kd2[g][2 * kk - 4]) : 0u;
+        const uint32_t w1 = ok ? (kk < 2 ? r.kd[g][2 * kk + 1] : r.kd2[g][2 * kk - 3]) : 0u;
+        uint32_t o4[4];
+        fp8x4_to_f16(w0, o4);
+        fp8x4_to_f16(w1, o4 + 2);
+        a = mfma16h(__builtin_bit_cast(f16x8, u32x4{o4[0], o4[1], o4[2], o4[3]}), qf[kk], a);
+      }
     }
     sc[g] = a;
   }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const bool ok = k + 16 * g + t16 < wk1;
-    const uint32_t vsw = ok ? r.vs[g] >> (16 * (q4 & 1)) : 0u;
-    const f16x2 sc2 = e4m3_pair_h<false>(vsw);
-    const f16x2 s0 = __builtin_shufflevector(sc2, sc2, 0, 0);
-    const f16x2 s1 = __builtin_shufflevector(sc2, sc2, 1, 1);
     uint32_t o[16];
-    dequant8_h(r.vd[g][0], s0, o + 0);
-    dequant8_h(r.vd[g][1], s0, o + 4);
-    dequant8_h(r.vd[g][2], s1, o + 8);
-    dequant8_h(r.vd[g][3], s1, o + 12);
+    if constexpr (FMT == kFmtNvfp4) {
+      const uint32_t vsw = ok ? r.vs[g] >> (16 * (q4 & 1)) : 0u;
+      const f16x2 sc2 = e4m3_pair_h<false>(vsw);
+      const f16x2 s0 = __builtin_shufflevector(sc2, sc2, 0, 0);
+      const f16x2 s1 = __builtin_shufflevector(sc2, sc2, 1, 1);
+      dequant8_h(r.vd[g][0], s0, o + 0);
+      dequant8_h(r.vd[g][1], s0, o + 4);
+      dequant8_h(r.vd[g][2], s1, o + 8);
+      dequant8_h(r.vd[g][3], s1, o + 12);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fp8x4_to_f16(ok ? r.vd[g][i] : 0u, o + 2 * i);
+        fp8x4_to_f16(ok ? r.vd2[g][i] : 0u, o + 8 + 2 * i);
+      }
+    }
     char* dst = stage + (16 * g + t16) * kDecVStride + 64 * q4;
     *(u32x4*)(dst + 0) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
@@ -156,6 +201,7 @@ __device__ __forceinline__ void decode_step(const DecodeRegs& r, int k, int wk1,
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <int FMT>
 __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kDecWaves * kDecStageBytes];
   __shared__ float red_m[kDecWaves][16];
@@ -241,7 +287,7 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
     asm volatile("v_mov_b32 %0, %1" : "=v"(pt1) : "v"(pt1_ld));
     // four register sets in rotation: the loads of three 32-token steps are in flight while
     // the fourth is consumed
-    DecodeRegs r0, r1, r2, r3;
+    DecodeRegs<FMT> r0, r1, r2, r3;
     decode_load(p, hk, wk0, wk1, pt0, pt1, wk0, lane, r0);
     decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + kDecStep, lane, r1);
     decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + 2 * kDecStep, lane, r2);
@@ -297,7 +343,10 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int items = p.num_kv_heads * p.batch * p.num_splits;
   const dim3 grid((unsigned)(8 * ((items + 7) / 8)));
-  hipLaunchKernelGGL(nvfp4_decode_kernel, grid, dim3(256), 0, stream, p);
+  if (p.fp8)
+    hipLaunchKernelGGL(nvfp4_decode_kernel<kFmtFp8>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(nvfp4_decode_kernel<kFmtNvfp4>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

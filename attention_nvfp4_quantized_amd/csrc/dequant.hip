@@ -6,7 +6,8 @@
 // of a wavefront converts the 32 values (16 packed bytes, two scale bytes) of quarter l%4 of
 // token l/4.  Each value is s * e2m1(code), exact in float32 (the fp4 conversion is exact and
 // the E4M3 scale is applied by one exact multiply), times g (one float32 rounding), then rounded
-// to nearest-even in the output type.  Slots < 0 give zero rows.
+// to nearest-even in the output type.  Slots < 0 give zero rows.  For the FP8 control cache a
+// value is e4m3(code) times g, rounded the same way.
 #include "device_common.hpp"
 #include "kernel_params.hpp"
 
@@ -22,7 +23,21 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(DequantParams p) {
   if (t >= p.num_tokens) return;
   const int64_t slot = p.slots[t];
   float x[32];
-  if (slot >= 0) {
+  if (slot >= 0 && p.fp8) {
+    // FP8 control cache: value = e4m3(code) * g (the conversion is exact)
+    const int64_t row = ((slot >> 4) * p.num_kv_heads + h) * kPageSize + (slot & 15);
+    const uint8_t* src = (which == 0 ? p.k_data : p.v_data) + row * kHeadDim + 32 * qq;
+    const u32x4 d0 = *(const u32x4*)src, d1 = *(const u32x4*)(src + 16);
+    const float g = which == 0 ? p.k_global : p.v_global;
+    const uint32_t wd[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);
+      x[4 * i] = lo[0] * g; x[4 * i + 1] = lo[1] * g;
+      x[4 * i + 2] = hi[0] * g; x[4 * i + 3] = hi[1] * g;
+    }
+  } else if (slot >= 0) {
     const int64_t row = ((slot >> 4) * p.num_kv_heads + h) * kPageSize + (slot & 15);
     const u32x4 d = *(const u32x4*)((which == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq);
     const uint32_t sw = *(const uint16_t*)((which == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq);

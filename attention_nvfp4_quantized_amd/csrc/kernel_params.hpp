@@ -21,6 +21,7 @@ struct AppendParams {
   int32_t num_tokens;
   int32_t num_kv_heads;
   int32_t fp16_in;  // input is IEEE binary16 (else bf16)
+  int32_t fp8;      // FP8 E4M3FN cache (else NVFP4)
 };
 
 struct DequantParams {
@@ -36,6 +37,7 @@ struct DequantParams {
   int32_t out_dtype;  // 0 bf16, 1 f32, 2 f16
   int32_t num_tokens;
   int32_t num_kv_heads;
+  int32_t fp8;        // FP8 E4M3FN cache (else NVFP4)
 };
 
 struct PrefillParams {
@@ -65,6 +67,7 @@ struct PrefillParams {
   int32_t out_f32;
   float* part_o;          // split mode: [num_splits][total_q][Hq][D]
   float* part_lse;        // split mode: [num_splits][total_q][Hq] (log2 units)
+  int32_t fp8;            // FP8 E4M3FN cache (else NVFP4)
 };
 
 struct MergeParams {
@@ -96,6 +99,7 @@ struct DecodeParams {
   float score_scale;
   float* part_o;          // [num_splits][batch][Hq][D]
   float* part_lse;        // [num_splits][batch][Hq]
+  int32_t fp8;            // FP8 E4M3FN cache (else NVFP4)
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

@@ -48,11 +48,17 @@ __device__ __forceinline__ int v_offset(int key, int slot) {
   return key * kVStride + 16 * (slot ^ (5 * (key & 3)));
 }
 
-template <int NW>
+// KV formats read by the prefill kernels: NVFP4 (packed E2M1 + E4M3 block scales) and the FP8
+// E4M3FN control cache (one byte per value, per-tensor scale only).
+constexpr int kFmtNvfp4 = 0;
+constexpr int kFmtFp8 = 1;
+
+template <int NW, int FMT>
 struct TileRegs {
-  static constexpr int kItems = 512 / (64 * NW);  // 16-byte chunks per thread per tile
-  u32x4 data[kItems];
-  uint32_t scale[kItems];
+  static constexpr int kItems = 512 / (64 * NW);  // 32-value chunks per thread per tile
+  u32x4 data[kItems];                              // NVFP4: 16 packed bytes; FP8: bytes 0-15
+  u32x4 data2[FMT == kFmtFp8 ? kItems : 1];        // FP8: bytes 16-31
+  uint32_t scale[FMT == kFmtNvfp4 ? kItems : 1];   // NVFP4: the chunk's two scale bytes
   int32_t page[kItems];  // page ids of the next tile to load (same value in every lane)
 };
 
@@ -62,12 +68,12 @@ struct TileRegs {
 // Fetch the page ids of tile `kt` with vector loads (one word, the same in every lane; `vzero`
 // is a zero the compiler cannot see as uniform, which keeps the loads off the scalar path, whose
 // wait would also drain the LDS queue).  Pages past the sequence's last page are clamped to it.
-template <int NW>
+template <int NW, int FMT>
 __device__ __forceinline__ void fetch_pages(const int32_t* bt_row, int kv_len, int kt, int vzero,
-                                            TileRegs<NW>& r) {
+                                            TileRegs<NW, FMT>& r) {
   const int last_page = (kv_len - 1) >> 4;
 #pragma unroll
-  for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
+  for (int j = 0; j < TileRegs<NW, FMT>::kItems; ++j) {
     const int sub = ((threadIdx.x + 64 * NW * j) & 255) >> 6;  // page of the tile, wave-uniform
     r.page[j] = bt_row[min(4 * kt + sub, last_page) + vzero];
   }
@@ -77,13 +83,13 @@ __device__ __forceinline__ void fetch_pages(const int32_t* bt_row, int kv_len, i
 // fetched for it, then fetch the page ids of tile `kt_next`.  Keys at or past kv_len are clamped
 // to the last key: every load is unconditional and reads written cache bytes, and those keys are
 // masked out of the softmax.
-template <int NW>
+template <int NW, int FMT>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t* bt_row, int hk,
                                           int kv_len, int kt, int kt_next, int vzero,
-                                          TileRegs<NW>& r) {
+                                          TileRegs<NW, FMT>& r) {
   const int last = kv_len - 1;
 #pragma unroll
-  for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
+  for (int j = 0; j < TileRegs<NW, FMT>::kItems; ++j) {
     const int it = threadIdx.x + 64 * NW * j;
     const int X = it >> 8;
     const int key = (it & 255) >> 2;
@@ -91,12 +97,18 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t*
     const int page = uniform(r.page[j]);
     const int gkey = min(kt * kTileKeys + key, last);
     const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (gkey & 15);
-    const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
-    const uint8_t* sp = (X == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq;
-    r.data[j] = *(const u32x4*)dp;
-    r.scale[j] = *(const uint16_t*)sp;
+    if constexpr (FMT == kFmtNvfp4) {
+      const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
+      const uint8_t* sp = (X == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq;
+      r.data[j] = *(const u32x4*)dp;
+      r.scale[j] = *(const uint16_t*)sp;
+    } else {
+      const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kHeadDim + 32 * qq;
+      r.data[j] = *(const u32x4*)dp;
+      r.data2[j] = *(const u32x4*)(dp + 16);
+    }
   }
-  fetch_pages<NW>(bt_row, kv_len, kt_next, vzero, r);
+  fetch_pages<NW, FMT>(bt_row, kv_len, kt_next, vzero, r);
 }
 
 // A zero held in a vector register that the compiler treats as lane-varying.
@@ -106,24 +118,38 @@ __device__ __forceinline__ int opaque_vzero() {
   return z;
 }
 
+// Four E4M3FN bytes -> four fp16 values (two words), exact.
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t out[2]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
 // Dequantize the loaded chunks to fp16 (exact) and write them to an LDS tile buffer.  The K / V
 // choice is made with selects, not branches, so the tile stages stay one scheduling region.
-template <int NW>
-__device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW>& r) {
+template <int NW, int FMT>
+__device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW, FMT>& r) {
 #pragma unroll
-  for (int j = 0; j < TileRegs<NW>::kItems; ++j) {
+  for (int j = 0; j < TileRegs<NW, FMT>::kItems; ++j) {
     const int it = threadIdx.x + 64 * NW * j;
     const bool is_v = (it >> 8) != 0;
     const int key = (it & 255) >> 2;
     const int qq = it & 3;
-    const f16x2 sc = e4m3_pair_h<false>(r.scale[j]);
-    const f16x2 s0 = __builtin_shufflevector(sc, sc, 0, 0);
-    const f16x2 s1 = __builtin_shufflevector(sc, sc, 1, 1);
     uint32_t o[16];
-    dequant8_h(r.data[j][0], s0, o + 0);
-    dequant8_h(r.data[j][1], s0, o + 4);
-    dequant8_h(r.data[j][2], s1, o + 8);
-    dequant8_h(r.data[j][3], s1, o + 12);
+    if constexpr (FMT == kFmtNvfp4) {
+      const f16x2 sc = e4m3_pair_h<false>(r.scale[j]);
+      const f16x2 s0 = __builtin_shufflevector(sc, sc, 0, 0);
+      const f16x2 s1 = __builtin_shufflevector(sc, sc, 1, 1);
+      dequant8_h(r.data[j][0], s0, o + 0);
+      dequant8_h(r.data[j][1], s0, o + 4);
+      dequant8_h(r.data[j][2], s1, o + 8);
+      dequant8_h(r.data[j][3], s1, o + 12);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fp8x4_to_f16(r.data[j][i], o + 2 * i);
+        fp8x4_to_f16(r.data2[j][i], o + 8 + 2 * i);
+      }
+    }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int off = is_v ? kKTileBytes + v_offset(key, 4 * qq + w) : key * kKStride + 64 * qq + 16 * w;
@@ -359,7 +385,7 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const P
 
 // ---- narrow kernel: NW wavefronts of 32 columns, two LDS buffers ---------------------------
 // Used for short query tiles (few columns), where the split-KV grid supplies the parallelism.
-template <int NW>
+template <int NW, int FMT>
 __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
   PrefillItem w;
@@ -384,15 +410,15 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
     const int vzero = opaque_vzero();
     const int t_last = w.t_end - 1;
     const int t0 = w.t_begin;
-    TileRegs<NW> r0, r1, r2;
-    fetch_pages<NW>(bt_row, w.kv_len, t0, vzero, r0);
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 3, t_last), vzero, r0);
-    fetch_pages<NW>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 4, t_last), vzero, r1);
-    fetch_pages<NW>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 5, t_last), vzero, r2);
-    store_tile<NW>(smem, r0);
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 6, t_last), vzero, r0);
+    TileRegs<NW, FMT> r0, r1, r2;
+    fetch_pages<NW, FMT>(bt_row, w.kv_len, t0, vzero, r0);
+    load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 3, t_last), vzero, r0);
+    fetch_pages<NW, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
+    load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 4, t_last), vzero, r1);
+    fetch_pages<NW, FMT>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
+    load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 5, t_last), vzero, r2);
+    store_tile<NW, FMT>(smem, r0);
+    load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 6, t_last), vzero, r0);
     __syncthreads();
     // One tile; register set R holds tile kt+1, which is written to the other buffer and then
     // reloaded with tile kt+4.
@@ -410,8 +436,8 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
       tile_probs(s0, s1, cs, m_used, pb, l_part);                                                  \
       tile_pv(buf, lane, pb, acc_o);                                                               \
     }                                                                                              \
-    store_tile<NW>(smem + ((kt + 1 - t0) & 1) * kBufBytes, R);                                     \
-    load_tile<NW>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 7, t_last), vzero, R); \
+    store_tile<NW, FMT>(smem + ((kt + 1 - t0) & 1) * kBufBytes, R);                                     \
+    load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 7, t_last), vzero, R); \
     __syncthreads();                                                                               \
   }
     int kt3 = t0;
@@ -439,6 +465,7 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
 // before the tile barrier, so tiles are dequantized two ahead into a third LDS buffer.
 constexpr int kStagWaves = 8;
 
+template <int FMT>
 __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[3 * kBufBytes];
   PrefillItem w;
@@ -463,16 +490,16 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
     const int vzero = opaque_vzero();
     const int t_last = w.t_end - 1;
     const int t0 = w.t_begin;
-    TileRegs<kStagWaves> ra, rb;
-    fetch_pages<kStagWaves>(bt_row, w.kv_len, t0, vzero, ra);
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 1, t_last), vzero, ra);
-    store_tile<kStagWaves>(smem, ra);
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 2, t_last), vzero, ra);
-    store_tile<kStagWaves>(smem + kBufBytes, ra);
+    TileRegs<kStagWaves, FMT> ra, rb;
+    fetch_pages<kStagWaves, FMT>(bt_row, w.kv_len, t0, vzero, ra);
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 1, t_last), vzero, ra);
+    store_tile<kStagWaves, FMT>(smem, ra);
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 2, t_last), vzero, ra);
+    store_tile<kStagWaves, FMT>(smem + kBufBytes, ra);
     __syncthreads();
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 4, t_last), vzero, ra);
-    fetch_pages<kStagWaves>(bt_row, w.kv_len, min(t0 + 3, t_last), vzero, rb);
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 5, t_last), vzero, rb);
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 4, t_last), vzero, ra);
+    fetch_pages<kStagWaves, FMT>(bt_row, w.kv_len, min(t0 + 3, t_last), vzero, rb);
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 5, t_last), vzero, rb);
 
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     if (ahead && t0 * kTileKeys <= c.wlim_max) tile_scores(smem, lane, qf, s0, s1);
@@ -496,8 +523,8 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
     }                                                                                              \
     /* unconditional, so every step has the same loads in flight; past the last tile the */      \
     /* writes land in a buffer that is not read again */                                           \
-    store_tile<kStagWaves>(bfill, R);                                                              \
-    load_tile<kStagWaves>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 6, t_last),    \
+    store_tile<kStagWaves, FMT>(bfill, R);                                                              \
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 6, t_last),    \
                           vzero, R);                                                               \
     if (ahead && kt + 1 < w.t_end && k0 + kTileKeys <= c.wlim_max)                                 \
       tile_scores(bnext, lane, qf, s0, s1);                                                        \
@@ -546,16 +573,22 @@ __global__ __launch_bounds__(256) void nvfp4_merge_kernel(MergeParams p) {
   if (p.lse && lane == 0) p.lse[row] = wsum > 0.0f ? (mx + __log2f(wsum)) * kLn2 : kNegInf;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_prefill_fmt(const PrefillParams& p, int waves, hipStream_t stream) {
   const dim3 grid((unsigned)(8 * p.items_per_xcd));
   switch (waves) {
-    case 8: hipLaunchKernelGGL(nvfp4_prefill_staggered_kernel, grid, dim3(512), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(nvfp4_prefill_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(nvfp4_prefill_kernel<2>, grid, dim3(128), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL(nvfp4_prefill_kernel<1>, grid, dim3(64), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL(nvfp4_prefill_staggered_kernel<FMT>, grid, dim3(512), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((nvfp4_prefill_kernel<4, FMT>), grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((nvfp4_prefill_kernel<2, FMT>), grid, dim3(128), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((nvfp4_prefill_kernel<1, FMT>), grid, dim3(64), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream) {
+  return p.fp8 ? launch_prefill_fmt<kFmtFp8>(p, waves, stream)
+               : launch_prefill_fmt<kFmtNvfp4>(p, waves, stream);
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {

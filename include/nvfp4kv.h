@@ -60,9 +60,21 @@ extern "C" {
 #define NVFP4KV_IN_BF16 0 /* writer input types of nvfp4_kv_append */
 #define NVFP4KV_IN_F16 1
 
+#define NVFP4KV_FORMAT_NVFP4 0 /* nvfp4kv_cache_t.kv_format */
+#define NVFP4KV_FORMAT_FP8 1
+
+/*
+ * FP8 control format (kv_format = NVFP4KV_FORMAT_FP8): the pages quote every NVFP4 result against
+ * an FP8 KV cache ([A] "Why NVFP4 KV cache A4Q prefill exists"; [B] "NVFP4 KV cache prefill vs
+ * decode performance").  Each value is one E4M3FN byte under the per-tensor scale g: the writer
+ * stores E4M3 round-to-nearest-even, saturating at 448, of fl32(x / g) with the sign bit copied,
+ * the reader multiplies by g.  X_data is uint8 [num_pages][num_kv_heads][16][head_dim]; there is
+ * no block-scale plane (k_scale / v_scale are ignored and may be NULL).  Every entry point below
+ * accepts either format through the descriptor.
+ */
 typedef struct nvfp4kv_cache {
-  uint8_t* k_data;  /* [num_pages][num_kv_heads][page_size][head_dim/2]  */
-  uint8_t* k_scale; /* [num_pages][num_kv_heads][page_size][head_dim/16] */
+  uint8_t* k_data;  /* [num_pages][num_kv_heads][page_size][head_dim/2]  (FP8: [..][head_dim]) */
+  uint8_t* k_scale; /* [num_pages][num_kv_heads][page_size][head_dim/16] (FP8: unused)         */
   uint8_t* v_data;
   uint8_t* v_scale;
   float k_global; /* per-tensor scales g (> 0, finite) */
@@ -72,6 +84,7 @@ typedef struct nvfp4kv_cache {
   int32_t num_kv_heads; /* >= 1 */
   int32_t head_dim;     /* must be 128; K and V head sizes are equal ([C] "The two controls are
                            independent in vLLM" notes the backend requires it) */
+  int32_t kv_format;    /* NVFP4KV_FORMAT_NVFP4 (0) or NVFP4KV_FORMAT_FP8 (1) */
 } nvfp4kv_cache_t;
 
 /*

@@ -12,6 +12,7 @@ import attention_nvfp4_quantized_amd as A
 import workload as W
 from oracle import attention as oattn
 from oracle import cache as ocache
+from oracle import fp8cache as ofp8
 
 DEV = "cuda"
 
@@ -39,10 +40,10 @@ def dev(x: np.ndarray) -> torch.Tensor:
 
 
 class GpuPrefillCase:
-    def __init__(self, pc: W.PrefillCase, k_global=1.0, v_global=1.0):
+    def __init__(self, pc: W.PrefillCase, k_global=1.0, v_global=1.0, kv_format="nvfp4"):
         self.pc, self.w = pc, pc.w
         self.cache = A.NVFP4KVCache(pc.layout.num_pages, pc.w.num_kv_heads, k_global=k_global,
-                                    v_global=v_global)
+                                    v_global=v_global, kv_format=kv_format)
         self.k, self.v = dev_bf16(pc.k_bits), dev_bf16(pc.v_bits)
         self.slots = dev(pc.slot_mapping)
         self.q = dev_bf16(pc.q_bits)
@@ -61,14 +62,19 @@ class GpuPrefillCase:
         return r
 
     def cache_host(self):
-        c = self.cache
-        return [t.cpu().numpy() for t in (c.k_data, c.k_scale, c.v_data, c.v_scale)]
+        return cache_planes(self.cache)
 
 
-def oracle_cache(pc: W.PrefillCase, seqs=None, k_global=1.0, v_global=1.0) -> ocache.PagedCache:
-    """Oracle cache holding the tokens of the given sequences (all by default)."""
-    c = ocache.PagedCache(pc.layout.num_pages, pc.w.num_kv_heads, k_global=k_global,
-                          v_global=v_global)
+def cache_planes(c: A.NVFP4KVCache):
+    """The cache's byte planes on the host, in the order ``assert_cache_equal`` compares."""
+    return [t.cpu().numpy() for t in (c.k_data, c.k_scale, c.v_data, c.v_scale) if t is not None]
+
+
+def oracle_cache(pc: W.PrefillCase, seqs=None, k_global=1.0, v_global=1.0, kv_format="nvfp4"):
+    """Oracle cache (NVFP4 or the FP8 control) holding the tokens of the given sequences (all
+    by default)."""
+    make = ofp8.Fp8PagedCache if kv_format == "fp8" else ocache.PagedCache
+    c = make(pc.layout.num_pages, pc.w.num_kv_heads, k_global=k_global, v_global=v_global)
     seqs = range(pc.w.batch) if seqs is None else seqs
     for b in seqs:
         s0, s1 = pc.cu_seqlens_kv[b], pc.cu_seqlens_kv[b + 1]
@@ -80,8 +86,10 @@ def seq_pages(layout: W.PageLayout, b: int) -> np.ndarray:
     return layout.block_table[b][: layout.pages_per_seq[b]]
 
 
-def assert_cache_equal(gpu_planes, oc: ocache.PagedCache, pages=None):
-    names = ("k_data", "k_scale", "v_data", "v_scale")
+def assert_cache_equal(gpu_planes, oc, pages=None):
+    names = ("k_data", "v_data") if isinstance(oc, ofp8.Fp8PagedCache) else (
+        "k_data", "k_scale", "v_data", "v_scale")
+    assert len(gpu_planes) == len(names)
     for name, g in zip(names, gpu_planes):
         o = getattr(oc, name)
         if pages is not None:
@@ -134,3 +142,50 @@ def oracle_prefill(pc: W.PrefillCase, oc: ocache.PagedCache, rows=None, causal=T
 
 def rows_of(pc: W.PrefillCase, seqs) -> np.ndarray:
     return np.concatenate([np.arange(pc.cu_seqlens_q[b], pc.cu_seqlens_q[b + 1]) for b in seqs])
+
+
+class DecodeRun:
+    """The decode workload at full size: 64 sequences, 64 steps of (append 64 tokens, decode).
+
+    Sampled sequences carry their seeded K/V; the others keep zero K/V, which changes none of
+    the sampled outputs (sequences are independent) and none of the launch shapes."""
+
+    def __init__(self, sampled, check_steps, kv_format="nvfp4"):
+        self.w = W.get("decode")
+        self.dc = W.decode_case(self.w)
+        self.kv_format = kv_format
+        lay, w = self.dc.layout, self.w
+        self.cache = A.NVFP4KVCache(lay.num_pages, w.num_kv_heads, kv_format=kv_format)
+        self.kv_bits = {b: self.dc.seq_kv(b) for b in sampled}
+        for b, (k, v) in self.kv_bits.items():
+            n = int(self.dc.init_lens[b]) - 1
+            A.append(self.cache, dev_bf16(k[:n]), dev_bf16(v[:n]), dev(lay.slots(b, np.arange(n))))
+        q_all = self.dc.step_q()
+        bt = dev(lay.block_table)
+        self.out = {}
+        max_kv = int(self.dc.init_lens.max()) + w.decode_steps - 1
+        zeros = np.zeros((w.batch, w.num_kv_heads, w.head_dim), np.uint16)
+        for t in range(w.decode_steps):
+            kb, vb = zeros.copy(), zeros.copy()
+            for b, (k, v) in self.kv_bits.items():
+                kb[b], vb[b] = k[int(self.dc.init_lens[b]) - 1 + t], v[int(self.dc.init_lens[b]) - 1 + t]
+            A.append(self.cache, dev_bf16(kb), dev_bf16(vb), dev(self.dc.step_slots(t)))
+            o = A.decode(self.cache, dev_bf16(q_all[t]), dev(self.dc.step_kv_lens(t)), bt, max_kv,
+                         w.sm_scale, out_dtype=torch.float32)
+            if t in check_steps:
+                self.out[t] = o.cpu().numpy()
+        torch.cuda.synchronize()
+        self.q_all = q_all
+
+    def oracle(self, steps, sampled):
+        """Oracle outputs at the given steps; its cache holds every token up to the last step
+        (a decode at step t reads only the first L_b + t of them)."""
+        lay = self.dc.layout
+        make = ofp8.Fp8PagedCache if self.kv_format == "fp8" else ocache.PagedCache
+        oc = make(lay.num_pages, self.w.num_kv_heads)
+        for b in sampled:
+            k, v = self.kv_bits[b]
+            n = int(self.dc.init_lens[b]) + max(steps)
+            oc.append(k[:n], v[:n], lay.slots(b, np.arange(n)))
+        return {t: oattn.decode(oc, self.q_all[t], self.dc.step_kv_lens(t), lay.block_table,
+                                self.w.sm_scale, seqs=sampled)[0] for t in steps}

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def _desc(**over):
     d = dict(k_data=16, k_scale=16, v_data=16, v_scale=16, k_global=1.0, v_global=1.0,
-             num_pages=4, page_size=16, num_kv_heads=8, head_dim=128)
+             num_pages=4, page_size=16, num_kv_heads=8, head_dim=128, kv_format=0)
     d.update(over)
     return CacheDesc(**d)
 
@@ -52,6 +52,8 @@ def _err():
     (dict(num_kv_heads=0), -1, "num_kv_heads"),
     (dict(k_global=0.0), -1, "global"),
     (dict(v_global=float("inf")), -1, "global"),
+    (dict(kv_format=2), -1, "kv_format"),
+    (dict(k_scale=None), -1, "NULL"),
 ])
 def test_append_rejects_bad_cache(over, code, needle):
     lib = load_library()
@@ -159,3 +161,24 @@ def test_binding_refuses_missing_library(tmp_path):
             B.load_library(str(tmp_path / "missing.so"))
     finally:
         B._lib = saved
+
+
+def test_fp8_format_needs_no_scale_plane():
+    """The FP8 control cache has no block scales: NULL scale pointers pass the checks (the
+    zero-token calls return before any launch)."""
+    lib = load_library()
+    d = _desc(kv_format=1, k_scale=None, v_scale=None)
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 0, 16, 0, None) == 0
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), 16, 0, 16, 16, 0, None) == 0
+    assert _prefill(lib, d, total_q=0) == 0
+    assert _err() == ""
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 512, 1024, 0, 16, 4, None) == -1
+
+
+def test_descriptor_layout_matches_header():
+    """The ctypes descriptor has the header's fields in the header's order."""
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct nvfp4kv_cache"):text.index("} nvfp4kv_cache_t;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\b([a-z_0-9]+);", body)
+    assert names == [f[0] for f in CacheDesc._fields_]

@@ -8,12 +8,10 @@ import numpy as np
 import pytest
 import torch
 
-import attention_nvfp4_quantized_amd as A
 import workload as W
-from oracle import attention as oattn
-from oracle import cache as ocache
-from gpu_cases import (LSE_ATOL, assert_attention_close_bf16, GpuPrefillCase, assert_attention_close, assert_cache_equal, dev, dev_bf16,
-                       oracle_cache, oracle_prefill, rows_of, say, seq_pages)
+from gpu_cases import (LSE_ATOL, DecodeRun, assert_attention_close_bf16, GpuPrefillCase,
+                       assert_attention_close, assert_cache_equal, oracle_cache, oracle_prefill,
+                       rows_of, say, seq_pages)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,51 +96,6 @@ def test_prefill_parity_tail16_sampled_sequences():
     seqs = [0, 5]
     ref, _ = oracle_prefill(pc, oracle_cache(pc, seqs), rows=rows_of(pc, seqs))
     assert_attention_close(o32, ref, "tail16 fp32")
-
-
-class DecodeRun:
-    """The decode workload at full size: 64 sequences, 64 steps of (append 64 tokens, decode).
-
-    Sampled sequences carry their seeded K/V; the others keep zero K/V, which changes none of
-    the sampled outputs (sequences are independent) and none of the launch shapes."""
-
-    def __init__(self, sampled, check_steps):
-        self.w = W.get("decode")
-        self.dc = W.decode_case(self.w)
-        lay, w = self.dc.layout, self.w
-        self.cache = A.NVFP4KVCache(lay.num_pages, w.num_kv_heads)
-        self.kv_bits = {b: self.dc.seq_kv(b) for b in sampled}
-        for b, (k, v) in self.kv_bits.items():
-            n = int(self.dc.init_lens[b]) - 1
-            A.append(self.cache, dev_bf16(k[:n]), dev_bf16(v[:n]), dev(lay.slots(b, np.arange(n))))
-        q_all = self.dc.step_q()
-        bt = dev(lay.block_table)
-        self.out = {}
-        max_kv = int(self.dc.init_lens.max()) + w.decode_steps - 1
-        zeros = np.zeros((w.batch, w.num_kv_heads, w.head_dim), np.uint16)
-        for t in range(w.decode_steps):
-            kb, vb = zeros.copy(), zeros.copy()
-            for b, (k, v) in self.kv_bits.items():
-                kb[b], vb[b] = k[int(self.dc.init_lens[b]) - 1 + t], v[int(self.dc.init_lens[b]) - 1 + t]
-            A.append(self.cache, dev_bf16(kb), dev_bf16(vb), dev(self.dc.step_slots(t)))
-            o = A.decode(self.cache, dev_bf16(q_all[t]), dev(self.dc.step_kv_lens(t)), bt, max_kv,
-                         w.sm_scale, out_dtype=torch.float32)
-            if t in check_steps:
-                self.out[t] = o.cpu().numpy()
-        torch.cuda.synchronize()
-        self.q_all = q_all
-
-    def oracle(self, steps, sampled):
-        """Oracle outputs at the given steps; its cache holds every token up to the last step
-        (a decode at step t reads only the first L_b + t of them)."""
-        lay = self.dc.layout
-        oc = ocache.PagedCache(lay.num_pages, self.w.num_kv_heads)
-        for b in sampled:
-            k, v = self.kv_bits[b]
-            n = int(self.dc.init_lens[b]) + max(steps)
-            oc.append(k[:n], v[:n], lay.slots(b, np.arange(n)))
-        return {t: oattn.decode(oc, self.q_all[t], self.dc.step_kv_lens(t), lay.block_table,
-                                self.w.sm_scale, seqs=sampled)[0] for t in steps}
 
 
 def test_decode_parity_full_size_sampled_sequences():
