@@ -5,11 +5,14 @@ cache followed by the causal paged prefill over it (32 query / 8 KV heads, head_
 size 16, shuffled pages).  ``value`` is the prefill's algorithmic FLOP rate over the whole step.
 The same run also times the 64-step decode loop (batch 64, 16K..32K cached tokens; each step
 appends one token per sequence and decodes) and reports decode microseconds per call and HBM
-GB/s, and times the CPU oracle on a bounded sample of the prefill workload.
+GB/s, and times the CPU oracle on a bounded sample of the prefill workload.  The FP8 control
+cache (one E4M3FN byte per value) is timed on the 16K prefill, the decode loop and the short
+prefill shapes, with NVFP4 / FP8 time ratios.
 
 Algorithmic work (nothing masked, padded or re-read is counted):
   prefill FLOP = 4 * head_dim * Hq * sum_b [q_b (kv_b - q_b) + q_b (q_b + 1) / 2]
-  decode bytes = sum_b kv_len_b * Hkv * 144 (K and V: 64 packed + 8 scale bytes each)
+  decode bytes = sum_b kv_len_b * Hkv * 144 (K and V: 64 packed + 8 scale bytes each;
+                 FP8 control: 256)
                  + Q and O (2 bytes * Hq * head_dim each per sequence)
   append bytes = tokens * Hkv * (2 * 2 * head_dim read + 2 * 72 written)
 Peaks: bf16 dense MFMA 2.5 PFLOP/s; HBM 8 TB/s (MI355X published figures).
@@ -37,9 +40,9 @@ METRIC = "NVFP4-KV causal prefill TFLOP/s @16K; decode µs/call & HBM GB/s"
 PEAK_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_full16k_prefill_decode_b64.json")
-PREFILL_KERNEL = "nvfp4_prefill_staggered_kernel"
+PREFILL_KERNEL = "nvfp4_prefill_staggered_kernel<0>"  # the NVFP4 instantiation
 PREFILL_SOURCES = ["prefill.hip", "device_common.hpp", "kernel_params.hpp"]
-DECODE_KERNEL = "nvfp4_decode_kernel"
+DECODE_KERNEL = "nvfp4_decode_kernel<0>"
 DECODE_SOURCES = ["decode.hip", "device_common.hpp", "kernel_params.hpp"]
 
 
@@ -76,8 +79,8 @@ def bf16_dev(bits, torch):
 
 
 def run_prefill(args, torch, A):
-    w = W.get("full16k")
-    pc = W.prefill_case(w)
+    pc = prefill_case("full16k")
+    w = pc.w
     cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
     k, v = bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch)
     slots = torch.from_numpy(pc.slot_mapping).cuda()
@@ -119,11 +122,17 @@ def run_prefill(args, torch, A):
                 prefill_ms=prefill_ms, append_bytes=append_bytes)
 
 
-def run_decode(args, torch, A):
+# cache bytes per (token, KV head) read by attention, K and V together
+KV_BYTES = {"nvfp4": 144, "fp8": 256}
+
+
+def run_decode(args, torch, A, formats=("nvfp4",)):
+    """The 64-step decode loop once per cache format (the same tokens in every cache); returns
+    one result dict per format."""
     w = W.get("decode")
     dc = W.decode_case(w)
     lay = dc.layout
-    cache = A.NVFP4KVCache(lay.num_pages, w.num_kv_heads)
+    caches = {f: A.NVFP4KVCache(lay.num_pages, w.num_kv_heads, kv_format=f) for f in formats}
     steps = w.decode_steps
     step_k = np.zeros((steps, w.batch, w.num_kv_heads, 128), np.uint16)
     step_v = np.zeros_like(step_k)
@@ -137,7 +146,9 @@ def run_decode(args, torch, A):
     workers = min(16, len(os.sched_getaffinity(0)))
     with cf.ThreadPoolExecutor(workers) as ex:
         for b, kb, vb, sl in ex.map(fill, range(w.batch)):
-            A.append(cache, bf16_dev(kb, torch), bf16_dev(vb, torch), torch.from_numpy(sl).cuda())
+            kd, vd, sd = bf16_dev(kb, torch), bf16_dev(vb, torch), torch.from_numpy(sl).cuda()
+            for cache in caches.values():
+                A.append(cache, kd, vd, sd)
     torch.cuda.synchronize()
     qs = bf16_dev(dc.step_q(), torch)
     ks, vs = bf16_dev(step_k, torch), bf16_dev(step_v, torch)
@@ -150,7 +161,7 @@ def run_decode(args, torch, A):
     ws = torch.empty(A.decode_workspace_size(w.batch, max_kv, w.num_qo_heads, w.num_kv_heads),
                      dtype=torch.uint8, device="cuda")
 
-    def loop(ev=None):
+    def loop(cache, ev=None):
         for t in range(steps):
             if ev is not None:
                 ev[t][0].record()
@@ -161,41 +172,63 @@ def run_decode(args, torch, A):
             if ev is not None:
                 ev[t][2].record()
 
-    # the warm-up pass rewrites the same step tokens, so the timed pass sees identical caches
-    loop()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    loop(ev)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    results = {}
+    for fmt, cache in caches.items():
+        # the warm-up pass rewrites the same step tokens, so the timed pass sees identical caches
+        loop(cache)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        loop(cache, ev)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        results[fmt] = decode_result(w, fmt, lens_np, ev, t1 - t0)
+    return results
+
+
+def decode_result(w, fmt, lens_np, ev, loop_s):
+    steps = len(ev)
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     app_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    bytes_per_step = (lens_np.sum(axis=1) * w.num_kv_heads * 144
+    bytes_per_step = (lens_np.sum(axis=1) * w.num_kv_heads * KV_BYTES[fmt]
                       + 2 * 2 * w.batch * w.num_qo_heads * 128).astype(np.float64)
     gbps = float(bytes_per_step.sum() / (dec_ms.sum() * 1e-3) / 1e9)
-    append_bytes = w.batch * w.num_kv_heads * (2 * 2 * 128 + 2 * 72)
-    return {
-        "workload": "decode", "batch": w.batch, "steps": steps,
+    append_bytes = w.batch * w.num_kv_heads * (2 * 2 * 128 + KV_BYTES[fmt])
+    out = {
+        "workload": "decode", "kv_format": fmt, "batch": w.batch, "steps": steps,
         "kv_len_min": int(lens_np.min()), "kv_len_max": int(lens_np.max()),
-        "loop_ms": round((t1 - t0) * 1e3, 3),
+        "loop_ms": round(loop_s * 1e3, 3),
         "us_per_call": round(float(dec_ms.mean()) * 1e3, 2),
         "bytes_per_call": int(bytes_per_step.mean()),
         "GBps": round(gbps, 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic("decode"), "kernel": DECODE_KERNEL},
         "append_us_per_call": round(float(app_ms.mean()) * 1e3, 2),
         "append_GBps": round(append_bytes / (app_ms.mean() * 1e-3) / 1e9, 1),
     }
+    if fmt == "nvfp4":
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                           "traffic": measured_traffic("decode"), "kernel": DECODE_KERNEL}
+    else:
+        out["hbm_frac"] = round(gbps / PEAK_HBM_GBPS, 4)
+    return out
 
 
-def run_full_prefill(name, torch, A, reps=8, warmup=4):
+_CASES = {}
+
+
+def prefill_case(name):
+    """Seeded host inputs of a prefill workload, generated once per run."""
+    if name not in _CASES:
+        _CASES[name] = W.prefill_case(W.get(name))
+    return _CASES[name]
+
+
+def run_full_prefill(name, torch, A, reps=8, warmup=4, kv_format="nvfp4"):
     """Kernel time of the append and the causal prefill of a full-length single request (the
     pages' benchmark matrix asks for full 8K and 32K prefill next to the tail shapes)."""
-    w = W.get(name)
-    pc = W.prefill_case(w)
-    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    pc = prefill_case(name)
+    w = pc.w
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads, kv_format=kv_format)
     k, v = bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch)
     slots = torch.from_numpy(pc.slot_mapping).cuda()
     q = bf16_dev(pc.q_bits, torch)
@@ -215,20 +248,20 @@ def run_full_prefill(name, torch, A, reps=8, warmup=4):
     pre = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     app = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
-    return {"workload": name, "q_len": int(w.q_lens[0]), "kv_len": int(w.kv_lens[0]),
-            "prefill_ms": round(pre, 4), "TFLOPs": round(flops / (pre * 1e-3) / 1e12, 2),
+    return {"workload": name, "kv_format": kv_format, "q_len": int(w.q_lens[0]),
+            "kv_len": int(w.kv_lens[0]), "prefill_ms": round(pre, 4), "TFLOPs": round(flops / (pre * 1e-3) / 1e12, 2),
             "mfma_frac": round(flops / (pre * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
             "append_us": round(app * 1e3, 2), "flop_per_call": flops}
 
 
-def run_short_prefill(name, torch, A, reps=20, warmup=5):
+def run_short_prefill(name, torch, A, reps=20, warmup=5, kv_format="nvfp4"):
     """Prefill-only timing of a short-query workload (tail128: 4 x 128 queries over 2,048 keys;
     tail16: 8 x 16 queries over 16,384 keys): median µs per call with a 512 MB buffer written
     between calls (flushing L2 and MALL, so the packed cache comes from HBM) and warm
     back-to-back, with algorithmic TFLOP/s and GB/s (Q + O + packed KV of every sequence)."""
-    w = W.get(name)
-    pc = W.prefill_case(w)
-    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    pc = prefill_case(name)
+    w = pc.w
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads, kv_format=kv_format)
     A.append(cache, bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch),
              torch.from_numpy(pc.slot_mapping).cuda())
     q = bf16_dev(pc.q_bits, torch)
@@ -259,9 +292,10 @@ def run_short_prefill(name, torch, A, reps=20, warmup=5):
         torch.cuda.synchronize()
         times[mode] = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
     flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
-    nbytes = float(sum(w.kv_lens) * w.num_kv_heads * 144 + 2 * 2 * pc.total_q * w.num_qo_heads * 128)
+    nbytes = float(sum(w.kv_lens) * w.num_kv_heads * KV_BYTES[kv_format]
+                   + 2 * 2 * pc.total_q * w.num_qo_heads * 128)
     t = times["flushed"] * 1e-3
-    return {"workload": name, "batch": w.batch, "q_len": int(w.q_lens[0]), "kv_len": int(w.kv_lens[0]),
+    return {"workload": name, "kv_format": kv_format, "batch": w.batch, "q_len": int(w.q_lens[0]), "kv_len": int(w.kv_lens[0]),
             "us_flushed": round(times["flushed"] * 1e3, 2), "us_warm": round(times["warm"] * 1e3, 2),
             "TFLOPs": round(flops / t / 1e12, 2), "mfma_frac": round(flops / t / 1e12 / PEAK_MFMA_TFLOPS, 4),
             "GBps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4),
@@ -299,6 +333,25 @@ def run_cpu_baseline(pc):
             "seconds": round(t_pre + t_append, 2)}
 
 
+def fp8_summary(line, fp8):
+    """The FP8 (E4M3FN, one byte per value) control cache timed on the same workloads, and the
+    NVFP4 / FP8 time ratios (above 1: NVFP4 slower)."""
+    out = dict(fp8)
+    pre = fp8["prefill_full16k"]
+    out["ratio_nvfp4_over_fp8"] = {
+        "prefill_full16k": round(line["roofline"]["kernel_ms"] / pre["prefill_ms"], 3),
+        "append_16k": round(line["append"]["us_per_call"] / pre["append_us"], 3),
+    }
+    if "decode" in fp8:
+        out["ratio_nvfp4_over_fp8"]["decode"] = round(
+            line["decode"]["us_per_call"] / fp8["decode"]["us_per_call"], 3)
+    for n, f in zip(line.get("short_prefill", []), fp8.get("short_prefill", [])):
+        out["ratio_nvfp4_over_fp8"][n["workload"] + "_flushed"] = round(n["us_flushed"] / f["us_flushed"], 3)
+    for n, f in zip(line.get("prefill_matrix", []), fp8.get("prefill_matrix", [])):
+        out["ratio_nvfp4_over_fp8"][n["workload"]] = round(n["prefill_ms"] / f["prefill_ms"], 3)
+    return out
+
+
 def copy_calibration(torch, nbytes=1 << 30):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -318,6 +371,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-short", action="store_true", help="skip the tail128 / tail16 prefill timings")
     ap.add_argument("--no-matrix", action="store_true", help="skip the full 8K / 32K prefill timings")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 control-cache timings")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -352,12 +406,25 @@ def main():
         "append": {"us_per_call": round(pre["append_ms"] * 1e3, 2), "tokens": 16384,
                    "GBps": round(pre["append_bytes"] / (pre["append_ms"] * 1e-3) / 1e9, 1)},
     }
+    fp8 = {}
     if not args.no_decode:
-        line["decode"] = run_decode(args, torch, A)
+        dec = run_decode(args, torch, A, ("nvfp4",) if args.no_fp8 else ("nvfp4", "fp8"))
+        line["decode"] = dec["nvfp4"]
+        if "fp8" in dec:
+            fp8["decode"] = dec["fp8"]
     if not args.no_short:
         line["short_prefill"] = [run_short_prefill(n, torch, A) for n in ("tail128", "tail16")]
+        if not args.no_fp8:
+            fp8["short_prefill"] = [run_short_prefill(n, torch, A, kv_format="fp8")
+                                    for n in ("tail128", "tail16")]
     if not args.no_matrix:
         line["prefill_matrix"] = [run_full_prefill(n, torch, A) for n in ("full8k", "full32k")]
+        if not args.no_fp8:
+            fp8["prefill_matrix"] = [run_full_prefill(n, torch, A, kv_format="fp8")
+                                     for n in ("full8k", "full32k")]
+    if not args.no_fp8:
+        fp8["prefill_full16k"] = run_full_prefill("full16k", torch, A, kv_format="fp8")
+        line["fp8_control"] = fp8_summary(line, fp8)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(pre["pc"])
     print(json.dumps(line))
