@@ -79,6 +79,24 @@ class PagedCache:
             out.append(codec.round_to_dtype(x, out_dtype))
         return out[0], out[1]
 
+    def repack(self, block_table: np.ndarray, kv_lens):
+        """Dequantize-ahead repack ("NVFP4 KV cache A4Q prefill explained", section "Compare A4Q
+        with dequantize-ahead repacking": each NVFP4 tile is converted once to FP16 before
+        attention uses it): every page holding keys 0..kv_lens[b]-1 of a sequence becomes
+        fp16 s * e2m1(code) (exact; the per-tensor scale g is left to the reader, as for the
+        packed cache).  Returns fp16 bit patterns (k, v), each [num_pages][num_kv_heads]
+        [page_size][head_dim]; pages no sequence reaches stay zero."""
+        bt = np.asarray(block_table, dtype=np.int64)
+        out = []
+        for data, scale in ((self.k_data, self.k_scale), (self.v_data, self.v_scale)):
+            o = np.zeros(data.shape[:-1] + (data.shape[-1] * 2,), np.uint16)
+            for b, n in enumerate(np.asarray(kv_lens, dtype=np.int64)):
+                pages = bt[b, : (int(n) + self.page_size - 1) // self.page_size]
+                x = codec.dequantize(data[pages], scale[pages])  # exact s * e2m1 in float64
+                o[pages] = codec.round_to_dtype(x.astype(np.float32), "fp16")
+            out.append(o)
+        return out[0], out[1]
+
     def gather(self, block_table_row: np.ndarray, n: int):
         """Dequantized K and V of positions 0..n-1 of one sequence: float64 [n][H][D]."""
         pos = np.arange(n)

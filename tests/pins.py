@@ -276,6 +276,27 @@ def check_fp8_dequant(codec, fp8_mod):
             assert not np.any(np.asarray(got[2], np.float64)), out
 
 
+def check_repack(codec, cache_mod, seed=9):
+    """The repacked fp16 copy decodes (by its fields) to the exact s * e2m1 of every element of
+    the reached pages, with g != 1 left out; pages beyond a sequence's length and pages no
+    sequence reaches stay zero."""
+    rng = np.random.default_rng(seed)
+    c = cache_mod.PagedCache(12, 2, k_global=1.5, v_global=0.75)
+    x = (rng.standard_normal((96, 2, 128)) * np.exp(rng.uniform(-8, 8, (96, 2, 1)))).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    c.append(bits, bits[::-1].copy(), np.arange(96, dtype=np.int64) + 16)  # pages 1..6
+    bt = np.array([[3, 1, 5, 0], [6, 4, 2, 9]], np.int32)
+    lens = [40, 33]  # sequence 0 reaches pages 3, 1, 5; sequence 1 reaches 6, 4, 2
+    k, v = c.repack(bt, lens)
+    reached = [3, 1, 5, 6, 4, 2]
+    for got, data, scale in ((k, c.k_data, c.k_scale), (v, c.v_data, c.v_scale)):
+        exact = codec.dequantize(data[reached], scale[reached])  # g = 1: the repack leaves g out
+        assert np.array_equal(fp16_value_by_fields(got[reached]), exact)
+        others = [p for p in range(12) if p not in reached]
+        assert not np.any(got[others])
+        assert np.any(exact)
+
+
 def check_worked_block(codec):
     g = golden("worked_block.json")
     x = np.array(g["values"], np.float32)

@@ -42,6 +42,10 @@ def test_dequant_routes_agree():
     pins.check_dequant_routes_agree(codec, cache)
 
 
+def test_repack_is_exact_fp16_of_the_block_values():
+    pins.check_repack(codec, cache)
+
+
 def test_worked_block():
     pins.check_worked_block(codec)
 
@@ -200,3 +204,14 @@ def test_pins_catch_dequant_without_scale():
     mod = types.SimpleNamespace(PagedCache=C)
     with pytest.raises(AssertionError):
         pins.check_dequant_routes_agree(codec, mod)
+
+
+def test_pins_catch_repack_applying_the_global_scale():
+    class C(cache.PagedCache):
+        def repack(self, block_table, kv_lens):
+            k, v = super().repack(block_table, kv_lens)
+            val = pins.fp16_value_by_fields(k) * self.k_global  # applies g, which the reader does
+            return codec.round_to_dtype(val.astype(np.float32), "fp16"), v
+    import types
+    with pytest.raises(AssertionError):
+        pins.check_repack(codec, types.SimpleNamespace(PagedCache=C))
