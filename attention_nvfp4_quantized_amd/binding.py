@@ -52,6 +52,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nvfp4_kv_append.restype = ctypes.c_int
     lib.nvfp4_kv_dequant.argtypes = [C, P, I32, P, P, I32, P]
     lib.nvfp4_kv_dequant.restype = ctypes.c_int
+    lib.nvfp4_kv_repack.argtypes = [C, C, P, I32, P, I32, I32, P]
+    lib.nvfp4_kv_repack.restype = ctypes.c_int
     lib.paged_prefill_nvfp4_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
     lib.paged_prefill_nvfp4_workspace_size.restype = SZ
     lib.paged_prefill_nvfp4.argtypes = [C, P, P, P, P, I32, I32, I32, I32, I32, I32, F, I32, P, I32,
@@ -82,7 +84,7 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-_FORMATS = {"nvfp4": 0, "fp8": 1}
+_FORMATS = {"nvfp4": 0, "fp8": 1, "f16": 2}
 
 
 class NVFP4KVCache:
@@ -90,15 +92,16 @@ class NVFP4KVCache:
 
     kv_format "nvfp4": packed E2M1 codes [pages][Hkv][16][64] plus E4M3 block scales
     [pages][Hkv][16][8] per K and V.  kv_format "fp8": the FP8 (E4M3FN) control cache, one byte
-    per value [pages][Hkv][16][128] and no scale plane."""
+    per value [pages][Hkv][16][128] and no scale plane.  kv_format "f16": the fp16 copy that
+    ``repack`` writes ([pages][Hkv][16][128] float16), read by ``prefill`` only."""
 
     def __init__(self, num_pages: int, num_kv_heads: int, device="cuda", k_global: float = 1.0,
                  v_global: float = 1.0, kv_format: str = "nvfp4"):
         if kv_format not in _FORMATS:
             raise ValueError(f"kv_format must be one of {sorted(_FORMATS)}, got {kv_format!r}")
         z = lambda s: torch.zeros(s, dtype=torch.uint8, device=device)  # noqa: E731
-        if kv_format == "fp8":
-            shape_d = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM)
+        if kv_format in ("fp8", "f16"):
+            shape_d = (num_pages, num_kv_heads, PAGE_SIZE, HEAD_DIM * (1 if kv_format == "fp8" else 2))
             self.k_data, self.v_data = z(shape_d), z(shape_d)
             self.k_scale = self.v_scale = None
         else:
@@ -164,6 +167,22 @@ def dequant(cache: NVFP4KVCache, slot_mapping: torch.Tensor, out_dtype=torch.bfl
                                            k.data_ptr(), v.data_ptr(), _OUT_DTYPES[out_dtype],
                                            _stream()))
     return k, v
+
+
+def repack(src: NVFP4KVCache, dst: NVFP4KVCache, block_table: torch.Tensor,
+           kv_lens: torch.Tensor, max_kv_len: int):
+    """nvfp4_kv_repack: convert every page that holds keys of the given sequences from the NVFP4
+    cache ``src`` into the fp16 copy ``dst`` (kv_format "f16", same pages, heads and global
+    scales); ``prefill(dst, ...)`` then reads the copy with the same block table."""
+    _need(block_table, torch.int32, "block_table"); _need(kv_lens, torch.int32, "kv_lens")
+    if not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError("block_table must be a contiguous [batch][stride] tensor")
+    if kv_lens.numel() != block_table.shape[0]:
+        raise ValueError("kv_lens must hold one length per block-table row")
+    s, d = src.desc(), dst.desc()
+    _check(load_library().nvfp4_kv_repack(ctypes.byref(s), ctypes.byref(d), block_table.data_ptr(),
+                                          block_table.shape[1], kv_lens.data_ptr(),
+                                          kv_lens.numel(), max_kv_len, _stream()))
 
 
 def prefill_workspace_size(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,

@@ -38,10 +38,11 @@ int check_launch(hipError_t e, const char* what) {
 
 int check_cache(const nvfp4kv_cache_t* c) {
   if (!c) return fail(NVFP4KV_EINVAL, "cache descriptor is NULL");
-  if (c->kv_format != NVFP4KV_FORMAT_NVFP4 && c->kv_format != NVFP4KV_FORMAT_FP8)
+  if (c->kv_format != NVFP4KV_FORMAT_NVFP4 && c->kv_format != NVFP4KV_FORMAT_FP8 &&
+      c->kv_format != NVFP4KV_FORMAT_F16)
     return fail(NVFP4KV_EINVAL, "kv_format %d unknown", c->kv_format);
-  const bool fp8 = c->kv_format == NVFP4KV_FORMAT_FP8;
-  if (!c->k_data || !c->v_data || (!fp8 && (!c->k_scale || !c->v_scale)))
+  const bool scales = c->kv_format == NVFP4KV_FORMAT_NVFP4;
+  if (!c->k_data || !c->v_data || (scales && (!c->k_scale || !c->v_scale)))
     return fail(NVFP4KV_EINVAL, "cache plane pointer is NULL");
   if (c->head_dim != 128)
     return fail(NVFP4KV_EUNSUPPORTED, "head_dim %d unsupported (K and V head size must be 128)",
@@ -52,6 +53,15 @@ int check_cache(const nvfp4kv_cache_t* c) {
   if (!(c->k_global > 0.0f) || !std::isfinite(c->k_global) || !(c->v_global > 0.0f) ||
       !std::isfinite(c->v_global))
     return fail(NVFP4KV_EINVAL, "global scales must be finite and > 0");
+  if (c->kv_format == NVFP4KV_FORMAT_F16 && (((uintptr_t)c->k_data | (uintptr_t)c->v_data) & 15u))
+    return fail(NVFP4KV_EINVAL, "fp16 cache planes must be 16-byte aligned");
+  return NVFP4KV_OK;
+}
+
+// The fp16 (repacked) format is written by the repack pass and read by the prefill only.
+int check_not_f16(const nvfp4kv_cache_t* c, const char* what) {
+  if (c->kv_format == NVFP4KV_FORMAT_F16)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s does not take the fp16 (repacked) cache format", what);
   return NVFP4KV_OK;
 }
 
@@ -117,6 +127,7 @@ int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
                     int64_t k_token_stride, int64_t v_token_stride, int32_t input_dtype,
                     const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
   if (int e = check_cache(cache)) return e;
+  if (int e = check_not_f16(cache, "nvfp4_kv_append")) return e;
   if (input_dtype != NVFP4KV_IN_BF16 && input_dtype != NVFP4KV_IN_F16)
     return fail(NVFP4KV_EINVAL, "input_dtype %d unknown", input_dtype);
   if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "num_tokens < 0");
@@ -150,6 +161,7 @@ int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
                      int32_t num_tokens, void* k_out, void* v_out, int32_t out_dtype,
                      void* stream) {
   if (int e = check_cache(cache)) return e;
+  if (int e = check_not_f16(cache, "nvfp4_kv_dequant")) return e;
   if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32 && out_dtype != NVFP4KV_OUT_F16)
     return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
   if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "num_tokens < 0");
@@ -171,6 +183,41 @@ int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
   p.num_kv_heads = cache->num_kv_heads;
   p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
   return check_launch(nvfp4kv::launch_dequant(p, (hipStream_t)stream), "dequant launch");
+}
+
+int nvfp4_kv_repack(const nvfp4kv_cache_t* src, const nvfp4kv_cache_t* dst,
+                    const int32_t* block_table, int32_t block_table_stride,
+                    const int32_t* kv_lens, int32_t batch, int32_t max_kv_len, void* stream) {
+  if (int e = check_cache(src)) return e;
+  if (int e = check_cache(dst)) return e;
+  if (src->kv_format != NVFP4KV_FORMAT_NVFP4)
+    return fail(NVFP4KV_EUNSUPPORTED, "repack source must be an NVFP4 cache");
+  if (dst->kv_format != NVFP4KV_FORMAT_F16)
+    return fail(NVFP4KV_EINVAL, "repack destination must have kv_format NVFP4KV_FORMAT_F16");
+  if (dst->num_pages != src->num_pages || dst->num_kv_heads != src->num_kv_heads ||
+      dst->k_global != src->k_global || dst->v_global != src->v_global)
+    return fail(NVFP4KV_EINVAL, "repack destination must match the source's pages, heads and global scales");
+  if (batch < 0 || max_kv_len < 0) return fail(NVFP4KV_EINVAL, "negative size");
+  if (batch > 65535) return fail(NVFP4KV_EINVAL, "batch %d above 65535", batch);
+  if (batch == 0 || max_kv_len == 0) return ok();
+  if (!block_table || !kv_lens) return fail(NVFP4KV_EINVAL, "block_table or kv_lens is NULL");
+  const int max_pages = (max_kv_len + 15) / 16;
+  if (block_table_stride < max_pages)
+    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
+                block_table_stride, max_kv_len);
+  nvfp4kv::RepackParams p{};
+  p.k_data = src->k_data;
+  p.k_scale = src->k_scale;
+  p.v_data = src->v_data;
+  p.v_scale = src->v_scale;
+  p.k_out = (uint16_t*)dst->k_data;
+  p.v_out = (uint16_t*)dst->v_data;
+  p.block_table = block_table;
+  p.kv_lens = kv_lens;
+  p.bt_stride = block_table_stride;
+  p.num_kv_heads = src->num_kv_heads;
+  return check_launch(nvfp4kv::launch_repack(p, batch, max_pages, (hipStream_t)stream),
+                      "repack launch");
 }
 
 size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
@@ -216,7 +263,11 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
     return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
   if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
 
-  const int nw = prefill_waves(max_q_len, g);
+  // The one-wave kernel holds three tiles of chunks in registers; the FP8 and fp16 chunks are
+  // two and four times the packed NVFP4 size and would spill there, so those formats take the
+  // two-wave kernel (a single query tile either way: the split count and workspace are the same).
+  int nw = prefill_waves(max_q_len, g);
+  if (nw == 1 && cache->kv_format != NVFP4KV_FORMAT_NVFP4) nw = 2;
   const int rows = 32 * nw / g;
   const int q_tiles = (max_q_len + rows - 1) / rows;
   const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);
@@ -224,7 +275,7 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
   if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
 
   nvfp4kv::PrefillParams p{};
-  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
+  p.format = cache->kv_format;
   p.k_data = cache->k_data;
   p.k_scale = cache->k_scale;
   p.v_data = cache->v_data;
@@ -291,6 +342,7 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
                        int32_t out_dtype, float* lse, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (int e = check_cache(cache)) return e;
+  if (int e = check_not_f16(cache, "paged_decode_nvfp4")) return e;
   if (batch < 0 || max_kv_len < 0) return fail(NVFP4KV_EINVAL, "negative size");
   if (batch == 0) return ok();
   if (!q || !kv_lens || !block_table || !out)

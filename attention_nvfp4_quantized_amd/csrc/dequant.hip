@@ -81,6 +81,47 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(DequantParams p) {
   }
 }
 
+// Dequantize-ahead repack ("NVFP4 KV cache A4Q prefill explained", section "Compare A4Q with
+// dequantize-ahead repacking": convert each NVFP4 tile once, before the attention kernel uses it
+// repeatedly): every page a sequence's keys occupy is converted to fp16 s * e2m1(code) (exact:
+// at most 5 significant bits, magnitude in [2^-10, 2688]) into a paged fp16 copy with the same
+// page ids.  The per-tensor scale g is not applied; the prefill over the copy applies it as it
+// does over the packed cache.  Grid: x = groups of 4 pages of a sequence, y = sequence,
+// z = KV head * 2 + (0 for K, 1 for V); a wavefront converts one page (lane l: quarter l%4 of
+// row l/4, 16 packed bytes and 2 scale bytes in, 64 bytes out).  A page shared by several
+// sequences is written with the same bytes by each.
+__global__ __launch_bounds__(256) void nvfp4_repack_kernel(RepackParams p) {
+  const int which = blockIdx.z & 1;
+  const int h = blockIdx.z >> 1;
+  const int b = blockIdx.y;
+  const int pi = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int kv_len = p.kv_lens[b];
+  if (pi * kPageSize >= kv_len) return;
+  const int lane = threadIdx.x & 63;
+  const int qq = lane & 3;
+  const int64_t page = p.block_table[(int64_t)b * p.bt_stride + pi];
+  const int64_t row = (page * p.num_kv_heads + h) * kPageSize + (lane >> 2);
+  const u32x4 d = *(const u32x4*)((which == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq);
+  const uint32_t sw = *(const uint16_t*)((which == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq);
+  const f16x2 sc = e4m3_pair_h<false>(sw);
+  const f16x2 s0 = __builtin_shufflevector(sc, sc, 0, 0);
+  const f16x2 s1 = __builtin_shufflevector(sc, sc, 1, 1);
+  uint32_t o[16];
+  dequant8_h(d[0], s0, o + 0);
+  dequant8_h(d[1], s0, o + 4);
+  dequant8_h(d[2], s1, o + 8);
+  dequant8_h(d[3], s1, o + 12);
+  uint16_t* dst = (which == 0 ? p.k_out : p.v_out) + row * kHeadDim + 32 * qq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *(u32x4*)(dst + 8 * i) = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+}
+
+hipError_t launch_repack(const RepackParams& p, int batch, int max_pages, hipStream_t stream) {
+  const dim3 grid((unsigned)((max_pages + 3) / 4), (unsigned)batch, (unsigned)(2 * p.num_kv_heads));
+  hipLaunchKernelGGL(nvfp4_repack_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.num_tokens + 63) / 64), (unsigned)(2 * p.num_kv_heads));
   switch (p.out_dtype) {

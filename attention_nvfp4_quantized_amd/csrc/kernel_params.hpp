@@ -67,7 +67,20 @@ struct PrefillParams {
   int32_t out_f32;
   float* part_o;          // split mode: [num_splits][total_q][Hq][D]
   float* part_lse;        // split mode: [num_splits][total_q][Hq] (log2 units)
-  int32_t fp8;            // FP8 E4M3FN cache (else NVFP4)
+  int32_t format;         // cache format: 0 NVFP4, 1 FP8 E4M3FN, 2 fp16 (repacked)
+};
+
+struct RepackParams {
+  const uint8_t* k_data;  // NVFP4 source planes
+  const uint8_t* k_scale;
+  const uint8_t* v_data;
+  const uint8_t* v_scale;
+  uint16_t* k_out;        // fp16 copy: [num_pages][num_kv_heads][16][128]
+  uint16_t* v_out;
+  const int32_t* block_table;
+  const int32_t* kv_lens;
+  int32_t bt_stride;
+  int32_t num_kv_heads;
 };
 
 struct MergeParams {
@@ -104,6 +117,7 @@ struct DecodeParams {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
+hipError_t launch_repack(const RepackParams& p, int batch, int max_pages, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

@@ -48,17 +48,21 @@ __device__ __forceinline__ int v_offset(int key, int slot) {
   return key * kVStride + 16 * (slot ^ (5 * (key & 3)));
 }
 
-// KV formats read by the prefill kernels: NVFP4 (packed E2M1 + E4M3 block scales) and the FP8
-// E4M3FN control cache (one byte per value, per-tensor scale only).
+// KV formats read by the prefill kernels: NVFP4 (packed E2M1 + E4M3 block scales), the FP8
+// E4M3FN control cache (one byte per value, per-tensor scale only), and the fp16 copy written by
+// the repack pass (values already dequantized; no conversion at tile load).
 constexpr int kFmtNvfp4 = 0;
 constexpr int kFmtFp8 = 1;
+constexpr int kFmtF16 = 2;
 
 template <int NW, int FMT>
 struct TileRegs {
   static constexpr int kItems = 512 / (64 * NW);  // 32-value chunks per thread per tile
-  u32x4 data[kItems];                              // NVFP4: 16 packed bytes; FP8: bytes 0-15
-  u32x4 data2[FMT == kFmtFp8 ? kItems : 1];        // FP8: bytes 16-31
-  uint32_t scale[FMT == kFmtNvfp4 ? kItems : 1];   // NVFP4: the chunk's two scale bytes
+  // 16-byte words per chunk: NVFP4 16 packed bytes, FP8 32 bytes, fp16 64 bytes
+  static constexpr int kWords = FMT == kFmtNvfp4 ? 1 : (FMT == kFmtFp8 ? 2 : 4);
+  static constexpr int kRowStride = FMT == kFmtNvfp4 ? kRowBytes : kHeadDim * kWords / 2;
+  u32x4 data[kItems][kWords];
+  uint32_t scale[FMT == kFmtNvfp4 ? kItems : 1];  // NVFP4: the chunk's two scale bytes
   int32_t page[kItems];  // page ids of the next tile to load (same value in every lane)
 };
 
@@ -97,15 +101,13 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t*
     const int page = uniform(r.page[j]);
     const int gkey = min(kt * kTileKeys + key, last);
     const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (gkey & 15);
+    constexpr int kW = TileRegs<NW, FMT>::kWords;
+    const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * TileRegs<NW, FMT>::kRowStride + 16 * kW * qq;
+#pragma unroll
+    for (int c = 0; c < kW; ++c) r.data[j][c] = *(const u32x4*)(dp + 16 * c);
     if constexpr (FMT == kFmtNvfp4) {
-      const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * qq;
       const uint8_t* sp = (X == 0 ? p.k_scale : p.v_scale) + row * kScaleBytes + 2 * qq;
-      r.data[j] = *(const u32x4*)dp;
       r.scale[j] = *(const uint16_t*)sp;
-    } else {
-      const uint8_t* dp = (X == 0 ? p.k_data : p.v_data) + row * kHeadDim + 32 * qq;
-      r.data[j] = *(const u32x4*)dp;
-      r.data2[j] = *(const u32x4*)(dp + 16);
     }
   }
   fetch_pages<NW, FMT>(bt_row, kv_len, kt_next, vzero, r);
@@ -139,16 +141,21 @@ __device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW, FMT>& r
       const f16x2 sc = e4m3_pair_h<false>(r.scale[j]);
       const f16x2 s0 = __builtin_shufflevector(sc, sc, 0, 0);
       const f16x2 s1 = __builtin_shufflevector(sc, sc, 1, 1);
-      dequant8_h(r.data[j][0], s0, o + 0);
-      dequant8_h(r.data[j][1], s0, o + 4);
-      dequant8_h(r.data[j][2], s1, o + 8);
-      dequant8_h(r.data[j][3], s1, o + 12);
-    } else {
+      dequant8_h(r.data[j][0][0], s0, o + 0);
+      dequant8_h(r.data[j][0][1], s0, o + 4);
+      dequant8_h(r.data[j][0][2], s1, o + 8);
+      dequant8_h(r.data[j][0][3], s1, o + 12);
+    } else if constexpr (FMT == kFmtFp8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fp8x4_to_f16(r.data[j][i], o + 2 * i);
-        fp8x4_to_f16(r.data2[j][i], o + 8 + 2 * i);
+        fp8x4_to_f16(r.data[j][0][i], o + 2 * i);
+        fp8x4_to_f16(r.data[j][1][i], o + 8 + 2 * i);
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[4 * c + i] = r.data[j][c][i];
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -580,15 +587,22 @@ hipError_t launch_prefill_fmt(const PrefillParams& p, int waves, hipStream_t str
     case 8: hipLaunchKernelGGL(nvfp4_prefill_staggered_kernel<FMT>, grid, dim3(512), 0, stream, p); break;
     case 4: hipLaunchKernelGGL((nvfp4_prefill_kernel<4, FMT>), grid, dim3(256), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((nvfp4_prefill_kernel<2, FMT>), grid, dim3(128), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((nvfp4_prefill_kernel<1, FMT>), grid, dim3(64), 0, stream, p); break;
+    case 1:  // NVFP4 only: the host gives the wider formats two waves
+      if constexpr (FMT != kFmtNvfp4) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((nvfp4_prefill_kernel<1, FMT>), grid, dim3(64), 0, stream, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream) {
-  return p.fp8 ? launch_prefill_fmt<kFmtFp8>(p, waves, stream)
-               : launch_prefill_fmt<kFmtNvfp4>(p, waves, stream);
+  switch (p.format) {
+    case kFmtNvfp4: return launch_prefill_fmt<kFmtNvfp4>(p, waves, stream);
+    case kFmtFp8: return launch_prefill_fmt<kFmtFp8>(p, waves, stream);
+    case kFmtF16: return launch_prefill_fmt<kFmtF16>(p, waves, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {

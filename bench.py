@@ -7,7 +7,9 @@ The same run also times the 64-step decode loop (batch 64, 16K..32K cached token
 appends one token per sequence and decodes) and reports decode microseconds per call and HBM
 GB/s, and times the CPU oracle on a bounded sample of the prefill workload.  The FP8 control
 cache (one E4M3FN byte per value) is timed on the 16K prefill, the decode loop and the short
-prefill shapes, with NVFP4 / FP8 time ratios.
+prefill shapes, with NVFP4 / FP8 time ratios; the dequantize-ahead repack (NVFP4 pages to an
+fp16 copy, then the prefill over the copy) is timed on the short shapes against the stock
+prefill.
 
 Algorithmic work (nothing masked, padded or re-read is counted):
   prefill FLOP = 4 * head_dim * Hq * sum_b [q_b (kv_b - q_b) + q_b (q_b + 1) / 2]
@@ -213,6 +215,54 @@ def decode_result(w, fmt, lens_np, ev, loop_s):
     return out
 
 
+def run_repack_prefill(name, torch, A, reps=20, warmup=5):
+    """Dequantize-ahead repack on a short-query workload: median µs of the repack pass (every
+    page the batch reads, NVFP4 -> fp16 copy), of the prefill over the copy, and of both
+    together, with a 512 MB buffer written before each call (cold caches), against the stock
+    prefill over the packed cache measured the same way."""
+    pc = prefill_case(name)
+    w = pc.w
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    A.append(cache, bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch),
+             torch.from_numpy(pc.slot_mapping).cuda())
+    dst = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads, kv_format="f16")
+    q = bf16_dev(pc.q_bits, torch)
+    cu = torch.from_numpy(pc.cu_seqlens_q).cuda()
+    kv = torch.from_numpy(pc.kv_lens).cuda()
+    bt = torch.from_numpy(pc.layout.block_table).cuda()
+    out = torch.empty((pc.total_q, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = A.prefill_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
+                                        w.num_qo_heads, w.num_kv_heads)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def prefill(c):
+        A.prefill(c, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        A.repack(cache, dst, bt, kv, pc.max_kv_len)
+        prefill(dst)
+        prefill(cache)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+    for i in range(reps):
+        flush.zero_()
+        ev[i][0].record()
+        A.repack(cache, dst, bt, kv, pc.max_kv_len)
+        ev[i][1].record()
+        prefill(dst)
+        ev[i][2].record()
+        flush.zero_()
+        ev[i][3].record()
+        prefill(cache)
+        ev[i][4].record()
+    torch.cuda.synchronize()
+    med = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in ev])) * 1e3  # noqa: E731
+    rep, pre, tot, stock = med(0, 1), med(1, 2), med(0, 2), med(3, 4)
+    return {"workload": name, "us_repack": round(rep, 2), "us_prefill_over_copy": round(pre, 2),
+            "us_repack_plus_prefill": round(tot, 2), "us_stock_prefill": round(stock, 2),
+            "ratio_repack_path_over_stock": round(tot / stock, 3)}
+
+
 _CASES = {}
 
 
@@ -369,7 +419,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-short", action="store_true", help="skip the tail128 / tail16 prefill timings")
+    ap.add_argument("--no-short", action="store_true",
+                    help="skip the tail128 / tail16 prefill timings (stock and repacked)")
     ap.add_argument("--no-matrix", action="store_true", help="skip the full 8K / 32K prefill timings")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 control-cache timings")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -417,6 +468,8 @@ def main():
         if not args.no_fp8:
             fp8["short_prefill"] = [run_short_prefill(n, torch, A, kv_format="fp8")
                                     for n in ("tail128", "tail16")]
+    if not args.no_short:
+        line["repack"] = [run_repack_prefill(n, torch, A) for n in ("tail128", "tail16")]
     if not args.no_matrix:
         line["prefill_matrix"] = [run_full_prefill(n, torch, A) for n in ("full8k", "full32k")]
         if not args.no_fp8:

@@ -62,6 +62,7 @@ extern "C" {
 
 #define NVFP4KV_FORMAT_NVFP4 0 /* nvfp4kv_cache_t.kv_format */
 #define NVFP4KV_FORMAT_FP8 1
+#define NVFP4KV_FORMAT_F16 2   /* fp16 copy written by nvfp4_kv_repack; read by prefill only */
 
 /*
  * FP8 control format (kv_format = NVFP4KV_FORMAT_FP8): the pages quote every NVFP4 result against
@@ -84,7 +85,8 @@ typedef struct nvfp4kv_cache {
   int32_t num_kv_heads; /* >= 1 */
   int32_t head_dim;     /* must be 128; K and V head sizes are equal ([C] "The two controls are
                            independent in vLLM" notes the backend requires it) */
-  int32_t kv_format;    /* NVFP4KV_FORMAT_NVFP4 (0) or NVFP4KV_FORMAT_FP8 (1) */
+  int32_t kv_format;    /* NVFP4KV_FORMAT_NVFP4 (0), NVFP4KV_FORMAT_FP8 (1) or
+                           NVFP4KV_FORMAT_F16 (2, see nvfp4_kv_repack) */
 } nvfp4kv_cache_t;
 
 /*
@@ -118,6 +120,27 @@ int nvfp4_kv_append(const nvfp4kv_cache_t* cache, const void* k, const void* v,
 int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
                      int32_t num_tokens, void* k_out, void* v_out, int32_t out_dtype,
                      void* stream);
+
+/*
+ * Dequantize-ahead repack ([A] "Compare A4Q with dequantize-ahead repacking": convert each NVFP4
+ * tile once before repeated MMA use, producing BF16 or FP16 K and V): convert every page that
+ * holds keys 0 .. kv_lens[b]-1 of each sequence b into an fp16 copy, for a prefill over that
+ * copy (paged_prefill_nvfp4 with `dst`).
+ *   src           NVFP4 cache (kv_format NVFP4KV_FORMAT_NVFP4).
+ *   dst           fp16 copy (kv_format NVFP4KV_FORMAT_F16): k_data / v_data are fp16
+ *                 [num_pages][num_kv_heads][16][head_dim] (256-byte rows, 16-byte aligned),
+ *                 scale planes unused (may be NULL); same num_pages, num_kv_heads and global
+ *                 scales as `src`.  A page keeps its id: the same block table addresses both.
+ *                 Values are s * e2m1(code), exact in fp16; g is not applied (the prefill applies
+ *                 it, as over the packed cache).  Pages no sequence reaches are not written.
+ *   block_table   int32 [batch][block_table_stride] (>= ceil(max_kv_len / 16)); kv_lens int32
+ *                 [batch], each <= max_kv_len.
+ * batch == 0 or max_kv_len == 0 is a no-op; batch must be <= 65535.  The fp16 format is read by
+ * paged_prefill_nvfp4 only; the other entry points reject it (NVFP4KV_EUNSUPPORTED).
+ */
+int nvfp4_kv_repack(const nvfp4kv_cache_t* src, const nvfp4kv_cache_t* dst,
+                    const int32_t* block_table, int32_t block_table_stride,
+                    const int32_t* kv_lens, int32_t batch, int32_t max_kv_len, void* stream);
 
 /*
  * Causal paged prefill over the NVFP4 cache with bf16 queries ([A] "Why NVFP4 KV cache A4Q

@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for n in ("nvfp4_kv_append", "nvfp4_kv_dequant", "paged_prefill_nvfp4", "paged_decode_nvfp4",
+    for n in ("nvfp4_kv_append", "nvfp4_kv_dequant", "nvfp4_kv_repack", "paged_prefill_nvfp4", "paged_decode_nvfp4",
               "paged_prefill_nvfp4_workspace_size", "paged_decode_nvfp4_workspace_size",
               "nvfp4kv_last_error", "nvfp4kv_version"):
         assert n in names, names
@@ -52,7 +52,7 @@ def _err():
     (dict(num_kv_heads=0), -1, "num_kv_heads"),
     (dict(k_global=0.0), -1, "global"),
     (dict(v_global=float("inf")), -1, "global"),
-    (dict(kv_format=2), -1, "kv_format"),
+    (dict(kv_format=3), -1, "kv_format"),
     (dict(k_scale=None), -1, "NULL"),
 ])
 def test_append_rejects_bad_cache(over, code, needle):
@@ -182,3 +182,35 @@ def test_descriptor_layout_matches_header():
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     names = re.findall(r"\b([a-z_0-9]+);", body)
     assert names == [f[0] for f in CacheDesc._fields_]
+
+
+def _repack(lib, src, dst, bt=16, bts=4, lens=16, batch=2, max_kv=64):
+    return lib.nvfp4_kv_repack(ctypes.byref(src), ctypes.byref(dst), bt, bts, lens, batch, max_kv, None)
+
+
+def test_repack_argument_checks():
+    lib = load_library()
+    src = _desc()
+    dst = _desc(kv_format=2, k_scale=None, v_scale=None)
+    assert _repack(lib, src, dst, batch=0) == 0 and _err() == ""
+    assert _repack(lib, src, dst, max_kv=0) == 0
+    assert _repack(lib, src, src) == -1 and "NVFP4KV_FORMAT_F16" in _err()
+    assert _repack(lib, dst, dst) == -2 and "source" in _err()
+    assert _repack(lib, _desc(kv_format=1, k_scale=None, v_scale=None), dst) == -2
+    assert _repack(lib, src, _desc(kv_format=2, num_pages=5)) == -1 and "match" in _err()
+    assert _repack(lib, src, _desc(kv_format=2, k_global=2.0)) == -1
+    assert _repack(lib, src, dst, bts=3) == -1 and "block_table_stride" in _err()
+    assert _repack(lib, src, dst, bt=None) == -1
+    assert _repack(lib, src, dst, batch=70000) == -1
+    assert _repack(lib, src, _desc(kv_format=2, k_data=24)) == -1 and "aligned" in _err()
+
+
+def test_f16_format_is_prefill_only():
+    lib = load_library()
+    d = _desc(kv_format=2, k_scale=None, v_scale=None)
+    assert lib.nvfp4_kv_append(ctypes.byref(d), 16, 16, 1024, 1024, 0, 16, 4, None) == -2
+    assert "fp16" in _err()
+    assert lib.nvfp4_kv_dequant(ctypes.byref(d), 16, 4, 16, 16, 0, None) == -2
+    assert lib.paged_decode_nvfp4(ctypes.byref(d), 16, 16, 16, 2048, 64, 32768, 32, 0.088, 16, 0,
+                                  None, 0, 16, 1 << 40, None) == -2
+    assert _prefill(lib, d, total_q=0) == 0

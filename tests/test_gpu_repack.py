@@ -1,0 +1,117 @@
+"""GPU parity of the dequantize-ahead repack: the fp16 copy is bit-exact against the oracle, and
+the prefill over the copy equals the prefill over the packed cache bit for bit (the same fp16
+tile values enter the same arithmetic) and meets the oracle bar (max-abs 1e-2, mean-abs 1e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import attention_nvfp4_quantized_amd as A
+import workload as W
+from gpu_cases import (GpuPrefillCase, assert_attention_close, dev, oracle_cache, oracle_prefill,
+                       rows_of, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _repacked(g: GpuPrefillCase):
+    c = g.cache
+    dst = A.NVFP4KVCache(c.num_pages, c.num_kv_heads, k_global=c.k_global, v_global=c.v_global,
+                         kv_format="f16")
+    A.repack(c, dst, g.bt, g.kv, g.pc.max_kv_len)
+    torch.cuda.synchronize()
+    return dst
+
+
+def _prefill(g, cache, out_dtype, num_splits=0, return_lse=False):
+    r = A.prefill(cache, g.q, g.cu, g.kv, g.bt, g.pc.max_q_len, g.pc.max_kv_len, g.w.sm_scale,
+                  out_dtype=out_dtype, return_lse=return_lse, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return r
+
+
+def _case(q_lens, kv_lens, hq=32, hkv=8, seed=3201, **kw):
+    return W.prefill_case(W.custom("case", q_lens, kv_lens, hq, hkv, seed, k_outlier_channels=4, **kw))
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail128"])
+def test_repack_bit_exact(name):
+    say(f"[repack] {name}")
+    pc = W.prefill_case(W.get(name))
+    g = GpuPrefillCase(pc)
+    g.append()
+    dst = _repacked(g)
+    ok, ov = oracle_cache(pc).repack(pc.layout.block_table, pc.kv_lens)
+    for got, exp, what in ((dst.k_data, ok, "k"), (dst.v_data, ov, "v")):
+        gh = got.cpu().numpy().view(np.uint16)
+        bad = np.argwhere(gh != exp)
+        assert len(bad) == 0, f"{what}: {len(bad)} values differ, first {bad[0].tolist()}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail128"])
+def test_prefill_over_repacked_copy(name):
+    say(f"[repack prefill] {name}")
+    pc = W.prefill_case(W.get(name))
+    g = GpuPrefillCase(pc)
+    g.append()
+    dst = _repacked(g)
+    o32, lse = _prefill(g, dst, torch.float32, return_lse=True)
+    s32, slse = _prefill(g, g.cache, torch.float32, return_lse=True)
+    assert torch.equal(o32, s32) and torch.equal(lse, slse)
+    assert torch.equal(_prefill(g, dst, torch.bfloat16), _prefill(g, g.cache, torch.bfloat16))
+    ref, _ = oracle_prefill(pc, oracle_cache(pc))
+    assert_attention_close(o32.cpu().numpy(), ref, f"repacked {name} fp32")
+
+
+@pytest.mark.parametrize("hq,hkv,gk,gv", [(8, 8, 1.0, 1.0), (16, 8, 1.0, 1.0), (32, 8, 1.5, 0.75),
+                                          (64, 8, 1.0, 1.0)])
+def test_repacked_every_kernel_width_and_split(hq, hkv, gk, gv):
+    """Every prefill kernel width (query-head groups 1, 2, 4, 8), forced key splits and non-unit
+    global scales: the copy gives the stock result bit for bit."""
+    say(f"[repack prefill] Hq {hq}, Hkv {hkv}, g ({gk}, {gv}), q lens [70, 41], kv lens [70, 300]")
+    pc = _case([70, 41], [70, 300], hq, hkv)
+    g = GpuPrefillCase(pc, k_global=gk, v_global=gv)
+    g.append()
+    dst = _repacked(g)
+    for splits in (0, 3):
+        assert torch.equal(_prefill(g, dst, torch.float32, splits), _prefill(g, g.cache, torch.float32, splits))
+    ref, _ = oracle_prefill(pc, oracle_cache(pc, k_global=gk, v_global=gv))
+    assert_attention_close(_prefill(g, dst, torch.float32).cpu().numpy(), ref, f"repacked Hq {hq}")
+
+
+def test_repacked_tail16_and_full16k():
+    """The benchmark's long-key shapes: tail16 (8 x 16 queries over 16K keys, sampled sequences
+    against the oracle) and the 16K full prefill (bitwise against the stock prefill)."""
+    for name in ("tail16", "full16k"):
+        say(f"[repack prefill] {name}")
+        pc = W.prefill_case(W.get(name))
+        g = GpuPrefillCase(pc)
+        g.append()
+        dst = _repacked(g)
+        o = _prefill(g, dst, torch.bfloat16)
+        assert torch.equal(o, _prefill(g, g.cache, torch.bfloat16))
+        if name == "tail16":
+            seqs = [0, 5]
+            ref, _ = oracle_prefill(pc, oracle_cache(pc, seqs), rows=rows_of(pc, seqs))
+            assert_attention_close(_prefill(g, dst, torch.float32).cpu().numpy(), ref, "repacked tail16")
+        del dst
+        torch.cuda.empty_cache()
+
+
+def test_repack_leaves_unreached_pages():
+    """Pages past a sequence's length and pages of no sequence are not written."""
+    say("[repack] shortened kv_lens")
+    pc = _case([5, 9], [70, 37], 8, 2, seed=3202)
+    g = GpuPrefillCase(pc)
+    g.append()
+    c = g.cache
+    dst = A.NVFP4KVCache(c.num_pages, c.num_kv_heads, kv_format="f16")
+    lens = np.array([20, 1], np.int32)  # sequence 0: pages 0, 1; sequence 1: page 0
+    A.repack(c, dst, g.bt, dev(lens), 40)
+    torch.cuda.synchronize()
+    bt = pc.layout.block_table
+    reached = sorted({int(bt[0, 0]), int(bt[0, 1]), int(bt[1, 0])})
+    ok, _ = oracle_cache(pc).repack(bt, lens)
+    got = dst.k_data.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ok)
+    others = [p for p in range(c.num_pages) if p not in reached]
+    assert not np.any(got[others])
