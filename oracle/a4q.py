@@ -1,0 +1,119 @@
+"""A4Q-style QK numerics, oracle side (test infrastructure; see the package docstring).
+
+"NVFP4 KV cache A4Q prefill explained", section "Quantize Q instead of expanding K": the A4Q
+kernel quantizes Q inside the kernel to block-scaled FP4 for the QK product, consumes K as the
+cache's packed E2M1 values with the cache's own block scales, and keeps PV in BF16.  Section
+"Make query accuracy a release gate" asks that the added error be measured across prompt
+lengths, head shapes, causal masks and scale outliers, and that the scale scheme, the grouping
+and the rounding be recorded.  The pages leave those choices open; each scheme below is a
+reading, named by what it does:
+
+* ``nvfp4``       16 consecutive head-dim values per block; block scale
+                  E4M3_RNE_sat(fl32(amax / 6)); elements E2M1 round-to-nearest-even, saturating
+                  at 6 (the cache writer's own rule applied to each query row; one scale level).
+* ``nvfp4_dual``  a float32 scale per (token, head) first, g = fl32(amax_row / (6 * 448)), so the
+                  row's largest block scale lands at the top of the E4M3 range; y = fl32(q / g);
+                  then the ``nvfp4`` rule on y; value g * s * e2m1 (two scale levels).
+* ``mxfp4``       32 consecutive values per block with a power-of-two scale
+                  X = 2^(floor(log2 amax) - 2) (the block's largest exponent minus E2M1's largest
+                  exponent, 2); elements E2M1 round-to-nearest-even of v / X, saturating at 6
+                  (the MX format; the one gfx950's block-scaled MFMA takes for its operands).
+
+The attention is the oracle's plain definition with each query row replaced by its quantized
+value (the QK product itself exact), K and V the cache's dequantized values, and the softmax
+weights rounded to bf16 (nearest-even) as the PV operand; the normaliser sums the unrounded
+weights (reading: only the PV operand is BF16).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codec
+from .cache import PagedCache
+
+SCHEMES = ("nvfp4", "nvfp4_dual", "mxfp4")
+MX_BLOCK = 32
+
+
+def _nvfp4_values(y32: np.ndarray) -> np.ndarray:
+    """Values g=1 NVFP4 quantization gives float32 rows y32 [..., D]: s * e2m1(code)."""
+    codes, sc = codec.quantize(y32)
+    return codec.dequantize(codec.pack(codes), sc)
+
+
+def mxfp4_values(x: np.ndarray) -> np.ndarray:
+    """MXFP4 quantization of float rows along the last axis (a multiple of 32 long): per block
+    X = 2^(floor(log2 amax) - 2), element E2M1_RNE_sat(v / X); returns X * e2m1 in float64.
+    A block of zeros stays zero."""
+    x = np.asarray(x, dtype=np.float64)
+    xb = x.reshape(*x.shape[:-1], x.shape[-1] // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(xb).max(axis=-1, keepdims=True)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+    # floor(log2) of a float64 can be off by one next to a power of two: settle it exactly
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > amax, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= amax, e + 1, e)
+    X = np.where(amax > 0, np.ldexp(1.0, (e - 2).astype(np.int64)), 0.0)
+    codes = codec.e2m1_encode(xb, X)
+    return (codec.e2m1_value(codes) * X).reshape(x.shape)
+
+
+def quantize_q(q: np.ndarray, scheme: str) -> np.ndarray:
+    """Quantized value of float query rows q [..., D] (exact bf16 values) under ``scheme``."""
+    q32 = np.asarray(q, dtype=np.float32)
+    if scheme == "nvfp4":
+        return _nvfp4_values(q32)
+    if scheme == "nvfp4_dual":
+        amax = np.abs(q32).max(axis=-1, keepdims=True)
+        g = (amax / np.float32(codec.E2M1_MAX * 448.0)).astype(np.float32)
+        g = np.where(g > 0, g, np.float32(1.0)).astype(np.float32)
+        y = (q32 / g).astype(np.float32)
+        return _nvfp4_values(y) * g.astype(np.float64)
+    if scheme == "mxfp4":
+        return mxfp4_values(q32)
+    raise ValueError(f"unknown scheme {scheme!r}")
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    return codec.bf16_to_f32(codec.round_to_dtype(np.asarray(x, np.float32), "bf16")).astype(np.float64)
+
+
+def attend_a4q(qh: np.ndarray, k: np.ndarray, v: np.ndarray, last_visible: np.ndarray,
+               sm_scale: float) -> np.ndarray:
+    """Rows of quantized queries qh [n][D] over k, v [m][D] (float64): scores exact, weights
+    rounded to bf16 for the PV product, normaliser from the unrounded weights."""
+    o = np.full((qh.shape[0], v.shape[1]), np.nan)
+    cols = np.arange(k.shape[0])
+    for r0 in range(0, qh.shape[0], 512):
+        r1 = min(qh.shape[0], r0 + 512)
+        z = sm_scale * (qh[r0:r1] @ k.T)
+        z[cols[None, :] > np.asarray(last_visible[r0:r1])[:, None]] = -np.inf
+        zmax = z.max(axis=1, initial=-np.inf)
+        ok = np.isfinite(zmax)
+        e = np.exp(z[ok] - zmax[ok, None])
+        o[r0:r1][ok] = (_round_bf16(e) @ v) / e.sum(axis=1)[:, None]
+    return o
+
+
+def prefill_a4q(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, block_table,
+                sm_scale: float, scheme: str, causal: bool = True, rows=None) -> np.ndarray:
+    """Causal paged prefill with A4Q-style QK (``scheme``); the arguments and the row selection
+    follow ``attention.prefill``.  Returns o [total_q][Hq][D] in float64 (NaN where not
+    evaluated)."""
+    q = codec.bf16_to_f32(q_bits).astype(np.float64)
+    total_q, hq, d = q.shape
+    group = hq // cache.num_kv_heads
+    o = np.full((total_q, hq, d), np.nan)
+    want = np.ones(total_q, bool) if rows is None else np.isin(np.arange(total_q), rows)
+    cu = np.asarray(cu_seqlens_q)
+    for b in range(len(kv_lens)):
+        q0, q1, kvl = int(cu[b]), int(cu[b + 1]), int(kv_lens[b])
+        idx = np.nonzero(want[q0:q1])[0]
+        if len(idx) == 0:
+            continue
+        kh, vh = cache.gather(block_table[b], kvl)
+        last = (kvl - (q1 - q0) + idx) if causal else np.full(len(idx), kvl - 1)
+        qq = quantize_q(q[q0 + idx], scheme)
+        for h in range(hq):
+            o[q0 + idx, h] = attend_a4q(qq[:, h], kh[:, h // group], vh[:, h // group], last, sm_scale)
+    return o
