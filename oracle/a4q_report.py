@@ -22,7 +22,7 @@ import time
 
 import numpy as np
 
-from . import a4q, attention, cache, codec
+from . import a4q, attention, cache
 
 
 def _cache_of(pc, seqs=None):
@@ -31,14 +31,6 @@ def _cache_of(pc, seqs=None):
         s0, s1 = pc.cu_seqlens_kv[b], pc.cu_seqlens_kv[b + 1]
         oc.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1])
     return oc
-
-
-def _q_outliers(q_bits: np.ndarray, seed: int, per_head: int = 4, factor: float = 8.0):
-    rng = np.random.default_rng(seed)
-    q = codec.bf16_to_f32(q_bits).copy()
-    for h in range(q.shape[1]):
-        q[:, h, rng.choice(q.shape[2], per_head, replace=False)] *= np.float32(factor)
-    return codec.round_to_dtype(q.astype(np.float32), "bf16")
 
 
 def cases():
@@ -52,7 +44,7 @@ def cases():
     yield "tiny, causal", tiny, tiny.q_bits, True, None, None
     yield "tail128, causal", t128, t128.q_bits, True, None, None
     yield "tail128, no mask", t128, t128.q_bits, False, None, None
-    yield "tail128, Q outlier channels x8", t128, _q_outliers(t128.q_bits, 77), True, None, None
+    yield "tail128, Q outlier channels x8", t128, W.scale_channels(t128.q_bits, 77, 4, 8.0), True, None, None
     yield "tail16, sequences 0 and 5", t16, t16.q_bits, True, rows_t16, [0, 5]
     yield "full16k, 24 rows", f16, f16.q_bits, True, np.linspace(0, 16383, 24).astype(np.int64), None
     yield "full32k, 24 rows", f32, f32.q_bits, True, np.linspace(0, 32767, 24).astype(np.int64), None

@@ -310,3 +310,27 @@ def decode_case(w: Workload) -> DecodeCase:
     lens = np.asarray(w.kv_lens, dtype=np.int64)
     layout = page_layout(w, capacity_lens=lens + w.decode_steps - 1)
     return DecodeCase(w, layout, lens.astype(np.int32))
+
+
+# ----------------------------------------------------------------------------------------
+# Stress transforms of seeded inputs (value-range edge cases; no method arithmetic)
+# ----------------------------------------------------------------------------------------
+
+def scale_channels(bits: np.ndarray, seed: int, per_head: int, factor: float) -> np.ndarray:
+    """bf16 patterns [T][H][D] with `per_head` seeded channels of every head multiplied by
+    `factor` (then rounded to bf16): outlier channels on the query side."""
+    rng = np.random.default_rng(seed)
+    x = bf16_bits_to_f32(bits).copy()
+    for h in range(x.shape[1]):
+        x[:, h, rng.choice(x.shape[2], per_head, replace=False)] *= np.float32(factor)
+    return f32_to_bf16_bits(x)
+
+
+def scale_tokens_pow2(bits: np.ndarray, seed: int, lo: int, hi: int) -> np.ndarray:
+    """bf16 patterns [T][H][D] with every token multiplied by its own seeded power of two
+    2^e, e uniform in [lo, hi] (exact in bf16 inside its range): a wide dynamic range of block
+    scales across tokens."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(lo, hi + 1, size=bits.shape[0]).astype(np.float32)
+    x = bf16_bits_to_f32(bits) * np.exp2(e)[:, None, None].astype(np.float32)
+    return f32_to_bf16_bits(x.astype(np.float32))
