@@ -165,18 +165,31 @@ __device__ __forceinline__ void store_tile(char* buf, const TileRegs<NW, FMT>& r
   }
 }
 
-// S^T (64 keys x this wave's 32 columns) for the K tile in `buf`.
+// S^T (64 keys x this wave's 32 columns) for the K tile in `buf`.  The K fragments of each
+// k-step are read two k-steps ahead of their MFMAs; scheduling barriers keep that order (left
+// alone, the compiler sinks every read next to its MFMA and each MFMA pair waits out a full
+// LDS round trip).
 __device__ __forceinline__ void tile_scores(const char* buf, int lane, const f16x8 (&qf)[8],
                                             f32x16& s0, f32x16& s1) {
   const char* kb = buf + (lane & 31) * kKStride + 16 * (lane >> 5);
   s0 = f32x16{};
   s1 = f32x16{};
+  f16x8 a0[2], a1[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    a0[t] = *(const f16x8*)(kb + 32 * t);
+    a1[t] = *(const f16x8*)(kb + 32 * kKStride + 32 * t);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const f16x8 a0 = *(const f16x8*)(kb + 32 * t);
-    const f16x8 a1 = *(const f16x8*)(kb + 32 * kKStride + 32 * t);
-    s0 = mfma32h(a0, qf[t], s0);
-    s1 = mfma32h(a1, qf[t], s1);
+    s0 = mfma32h(a0[t & 1], qf[t], s0);
+    s1 = mfma32h(a1[t & 1], qf[t], s1);
+    if (t + 2 < 8) {
+      a0[t & 1] = *(const f16x8*)(kb + 32 * (t + 2));
+      a1[t & 1] = *(const f16x8*)(kb + 32 * kKStride + 32 * (t + 2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
