@@ -92,7 +92,7 @@ struct DecodeState {
 };
 
 // One 32-token step: scores, V staging, online softmax, PV.
-template <int FMT>
+template <int FMT, bool FULL>
 __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int wk1, int lane,
                                             const f16x8 (&qf)[4], float cs, char* stage,
                                             DecodeState& st) {
@@ -101,7 +101,7 @@ __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int
   f32x4 sc[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const bool ok = k + 16 * g + t16 < wk1;  // this lane's token is in range
+    const bool ok = FULL || k + 16 * g + t16 < wk1;  // this lane's token is in range
     f32x4 a = f32x4{};
     if constexpr (FMT == kFmtNvfp4) {
       const uint32_t ksw = ok ? r.ks[g] >> (16 * (q4 & 1)) : 0u;
@@ -129,7 +129,7 @@ __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int
   }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const bool ok = k + 16 * g + t16 < wk1;
+    const bool ok = FULL || k + 16 * g + t16 < wk1;
     uint32_t o[16];
     if constexpr (FMT == kFmtNvfp4) {
       const uint32_t vsw = ok ? r.vs[g] >> (16 * (q4 & 1)) : 0u;
@@ -153,11 +153,13 @@ __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int
     *(u32x4*)(dst + 32) = u32x4{o[8], o[9], o[10], o[11]};
     *(u32x4*)(dst + 48) = u32x4{o[12], o[13], o[14], o[15]};
   }
+  if constexpr (!FULL) {
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (k + 16 * g + 4 * q4 + j >= wk1) sc[g][j] = kNegInf;
+      for (int j = 0; j < 4; ++j)
+        if (k + 16 * g + 4 * q4 + j >= wk1) sc[g][j] = kNegInf;
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[0][j], sc[1][j]));
@@ -291,18 +293,27 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
     decode_load(p, hk, wk0, wk1, pt0, pt1, wk0, lane, r0);
     decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + kDecStep, lane, r1);
     decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + 2 * kDecStep, lane, r2);
-#define NVFP4KV_DECODE_STAGE(CUR, NXT, OFF)                                          \
+#define NVFP4KV_DECODE_STAGE(CUR, NXT, OFF, FULL)                                    \
   {                                                                                  \
     decode_load(p, hk, wk0, wk1, pt0, pt1, k + (OFF) + 3 * kDecStep, lane, NXT);    \
     __builtin_amdgcn_sched_barrier(0);                                               \
-    decode_step(CUR, k + (OFF), wk1, lane, qf, cs, stage, st);                       \
+    decode_step<FMT, FULL>(CUR, k + (OFF), wk1, lane, qf, cs, stage, st);            \
     __builtin_amdgcn_sched_barrier(0);                                               \
   }
-    for (int k = wk0; k < wk1; k += 4 * kDecStep) {
-      NVFP4KV_DECODE_STAGE(r0, r3, 0)
-      NVFP4KV_DECODE_STAGE(r1, r0, kDecStep)
-      NVFP4KV_DECODE_STAGE(r2, r1, 2 * kDecStep)
-      NVFP4KV_DECODE_STAGE(r3, r2, 3 * kDecStep)
+    // groups of four steps wholly inside [wk0, wk1) skip every range check; the last group
+    // masks the keys past wk1
+    int k = wk0;
+    for (; k + 4 * kDecStep <= wk1; k += 4 * kDecStep) {
+      NVFP4KV_DECODE_STAGE(r0, r3, 0, true)
+      NVFP4KV_DECODE_STAGE(r1, r0, kDecStep, true)
+      NVFP4KV_DECODE_STAGE(r2, r1, 2 * kDecStep, true)
+      NVFP4KV_DECODE_STAGE(r3, r2, 3 * kDecStep, true)
+    }
+    if (k < wk1) {
+      NVFP4KV_DECODE_STAGE(r0, r3, 0, false)
+      NVFP4KV_DECODE_STAGE(r1, r0, kDecStep, false)
+      NVFP4KV_DECODE_STAGE(r2, r1, 2 * kDecStep, false)
+      NVFP4KV_DECODE_STAGE(r3, r2, 3 * kDecStep, false)
     }
 #undef NVFP4KV_DECODE_STAGE
   }
