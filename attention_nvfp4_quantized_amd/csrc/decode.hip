@@ -20,6 +20,10 @@
 //  * The four wavefronts are combined in LDS; one partial (o, log2-sum-exp) per (sequence, query
 //    head, slice) goes to the workspace, and a merge kernel reduces the slices.
 //  * The workgroup -> (KV head, sequence, slice) map keeps each KV head on one XCD.
+//  * Only a wavefront's last group of four steps can hold tokens past its range; the groups
+//    before it run without any per-token range selects or score masks.
+//  * The same kernel reads the FP8 (E4M3FN) control cache (FMT = 1): 32 bytes per lane and
+//    token, one conversion per pair of values and no block scales.
 #include "device_common.hpp"
 #include "kernel_params.hpp"
 

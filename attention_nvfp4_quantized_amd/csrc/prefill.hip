@@ -27,6 +27,8 @@
 //    rows cannot see a tile skip its MFMAs; masks are applied only on tiles that need them.
 //  * The workgroup -> work-item map sends all work of one KV head to one XCD (its L2 holds that
 //    head's packed cache) and orders query tiles longest first.
+//  * The kernels are templated on the cache format: NVFP4, the FP8 (E4M3FN) control cache, and
+//    the fp16 copy the dequantize-ahead repack pass writes (stored to LDS without conversion).
 #include "device_common.hpp"
 #include "kernel_params.hpp"
 

@@ -28,6 +28,7 @@ import concurrent.futures as cf
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,10 +55,14 @@ def prefill_flops(q_lens, kv_lens, hq, d=128) -> float:
 
 
 def source_hash(files) -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so that a change of
+    code, not of commentary, marks the committed counters as stale."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "attention_nvfp4_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "attention_nvfp4_quantized_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
