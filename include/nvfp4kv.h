@@ -122,10 +122,10 @@ int nvfp4_kv_dequant(const nvfp4kv_cache_t* cache, const int64_t* slot_mapping,
                      void* stream);
 
 /*
- * Dequantize-ahead repack ([A] "Compare A4Q with dequantize-ahead repacking": convert each NVFP4
- * tile once before repeated MMA use, producing BF16 or FP16 K and V): convert every page that
- * holds keys 0 .. kv_lens[b]-1 of each sequence b into an fp16 copy, for a prefill over that
- * copy (paged_prefill_nvfp4 with `dst`).
+ * Dequantize-ahead repack ([A] "Compare A4Q with dequantize-ahead repacking": the NVFP4 data is
+ * widened to 16-bit floats a single time, ahead of the matrix products that reuse it): convert
+ * every page that holds keys 0 .. kv_lens[b]-1 of each sequence b into an fp16 copy, for a
+ * prefill over that copy (paged_prefill_nvfp4 with `dst`).
  *   src           NVFP4 cache (kv_format NVFP4KV_FORMAT_NVFP4).
  *   dst           fp16 copy (kv_format NVFP4KV_FORMAT_F16): k_data / v_data are fp16
  *                 [num_pages][num_kv_heads][16][head_dim] (256-byte rows, 16-byte aligned),

@@ -1,9 +1,9 @@
 """Added output error of A4Q-style QK (``oracle/a4q.py``) against the stock read path, on the
 seeded workloads (test infrastructure; CPU only).
 
-"NVFP4 KV cache A4Q prefill explained", section "Make query accuracy a release gate": measure
-the attention outputs against a wide reference across prompt lengths, head shapes, causal masks
-and scale outliers.  Both sides read the same oracle NVFP4 cache; the reference is the oracle's
+"NVFP4 KV cache A4Q prefill explained", section "Make query accuracy a release gate": the error
+a quantized query adds to the attention output is to be measured against a high-precision
+reference over varied sequence lengths, head layouts, masking and outlier scales.  Both sides read the same oracle NVFP4 cache; the reference is the oracle's
 float64 attention with the bf16 queries as given.  Cases:
 
 * tiny (q = kv = 256, 4/1 heads, 2 K outlier channels), causal;
