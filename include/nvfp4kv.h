@@ -177,8 +177,8 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
                         void* stream);
 
 /*
- * Single-token paged decode ([B] "Decode can win on fewer bytes read": decode reads the growing
- * cache for one new token after appending its K/V).  Split-KV: each (sequence, KV head, split)
+ * Single-token paged decode ([B] "Decode can win on fewer bytes read": each step scans the whole
+ * cache of a sequence for its one new query, after that token's K/V has been written).  Split-KV: each (sequence, KV head, split)
  * computes a partial softmax over its slice of the cache; a merge combines the partials.
  *   q        bf16 [batch][num_qo_heads][head_dim]; query b sees all kv_lens[b] keys.
  *   out      [batch][num_qo_heads][head_dim] bf16 or float32; lse as for prefill.

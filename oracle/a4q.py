@@ -1,12 +1,12 @@
 """A4Q-style QK numerics, oracle side (test infrastructure; see the package docstring).
 
 "NVFP4 KV cache A4Q prefill explained", section "Quantize Q instead of expanding K": the A4Q
-kernel quantizes Q inside the kernel to block-scaled FP4 for the QK product, consumes K as the
-cache's packed E2M1 values with the cache's own block scales, and keeps PV in BF16.  Section
-"Make query accuracy a release gate" asks that the added error be measured across prompt
-lengths, head shapes, causal masks and scale outliers, and that the scale scheme, the grouping
-and the rounding be recorded.  The pages leave those choices open; each scheme below is a
-reading, named by what it does:
+kernel turns Q into block-scaled FP4 in the kernel for the QK product, feeds the packed K codes
+and their stored block scales to that product unchanged, and does PV in BF16.  Section "Make
+query accuracy a release gate" asks for the added error over varied sequence lengths, head
+layouts, masking and outlier scales, with the scale scheme, block grouping and rounding
+written down.  The pages leave those choices open; each scheme below is a reading, named by
+what it does:
 
 * ``nvfp4``       16 consecutive head-dim values per block; block scale
                   E4M3_RNE_sat(fl32(amax / 6)); elements E2M1 round-to-nearest-even, saturating

@@ -6,8 +6,9 @@ converted and scaled back to values, and attention runs with bf16 queries
 prefill explained" and "Why NVFP4 KV cache A4Q prefill exists"; "NVFP4 KV
 cache prefill vs decode performance", section "Cold prefill can lose on
 conversion cost").  Prefill writes the chunk's K/V into the cache and then
-reads every key, the chunk's own included, from the cache; decode reads the
-growing cache for one new token after its K/V has been appended ("NVFP4 KV
+reads every key, the chunk's own included, from the cache; decode scans the
+whole cache of a sequence for its single newest query, after that token's K/V
+has been written ("NVFP4 KV
 cache prefill vs decode performance", section "NVFP4 KV cache prefill vs
 decode performance").
 

@@ -1,7 +1,7 @@
 """Paged NVFP4 KV cache, oracle side (test infrastructure; see the package docstring).
 
 The cache writer quantizes bf16 K/V vectors, chooses block scales, packs the
-codes and maps the result into paged cache slots ("NVFP4 KV cache prefill vs
+codes and stores each token's row at its slot in the page pool ("NVFP4 KV cache prefill vs
 decode performance", section "NVFP4 stores 4.5 bits per value before
 padding"; "NVFP4 KV cache vs NVFP4 weights", section "The cache quantizes
 values during serving").  The block-scale plane is kept linear (row-major,

@@ -8,8 +8,8 @@ Formats, as the pages define them:
   performance", section "NVFP4 stores 4.5 bits per value before padding";
   "NVFP4 KV cache vs NVFP4 weights", section "NVFP4 KV cache vs NVFP4
   weights");
-* a second, per-tensor scale ``g`` maps the tensor into the range that the
-  FP4 values and their block scales represent (same page and section).
+* a second, per-tensor scale ``g`` brings the tensor into the range that
+  E2M1 codes under E4M3 block scales can cover (same page and section).
 
 Readings where the pages are silent (each is listed in the design notes):
 
