@@ -34,9 +34,6 @@ constexpr int kDecStep = 32;
 constexpr int kDecVStride = 288;  // bytes per staged V row (256 + 32 pad for transposed reads)
 constexpr int kDecStageBytes = kDecStep * kDecVStride;
 
-constexpr int kFmtNvfp4 = 0;  // packed E2M1 + E4M3 block scales
-constexpr int kFmtFp8 = 1;    // E4M3FN control cache: one byte per value, per-tensor scale only
-
 // One lane's share of a 32-token step: 32 head-dim values of one token in each of two 16-token
 // groups, for K and V (NVFP4: 16 packed bytes plus the dword holding two scale bytes; FP8: 32
 // bytes).
@@ -46,12 +43,6 @@ struct DecodeRegs {
   u32x4 kd2[FMT == kFmtFp8 ? 2 : 1], vd2[FMT == kFmtFp8 ? 2 : 1];
   uint32_t ks[FMT == kFmtNvfp4 ? 2 : 1], vs[FMT == kFmtNvfp4 ? 2 : 1];
 };
-
-// Four E4M3FN bytes -> four fp16 values (two words), exact.
-__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t out[2]) {
-  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-}
 
 // Page id of the wave-relative page index `pi` (uniform, < 128) from the two page-id registers.
 __device__ __forceinline__ int page_at(int pt0, int pt1, int pi) {

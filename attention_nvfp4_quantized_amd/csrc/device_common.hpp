@@ -113,6 +113,19 @@ __device__ __forceinline__ void dequant8_h(uint32_t word, f16x2 s, uint32_t out[
   out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s);
 }
 
+// Four E4M3FN bytes -> four fp16 values (two words), exact (every E4M3 value is an fp16 value).
+__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t out[2]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+// Cache formats the attention kernels read (template argument FMT): NVFP4 (packed E2M1 codes
+// plus E4M3 block scales), the FP8 E4M3FN control cache (one byte per value, per-tensor scale
+// only), and the fp16 copy the dequantize-ahead repack pass writes (prefill only).
+constexpr int kFmtNvfp4 = 0;
+constexpr int kFmtFp8 = 1;
+constexpr int kFmtF16 = 2;
+
 // Two floats -> fp16 pair, rounded toward zero (relative error < 2^-10).
 __device__ __forceinline__ f16x2 pack_f16x2_rtz(float lo, float hi) {
   return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo, hi));

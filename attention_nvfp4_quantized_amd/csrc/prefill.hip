@@ -50,13 +50,6 @@ __device__ __forceinline__ int v_offset(int key, int slot) {
   return key * kVStride + 16 * (slot ^ (5 * (key & 3)));
 }
 
-// KV formats read by the prefill kernels: NVFP4 (packed E2M1 + E4M3 block scales), the FP8
-// E4M3FN control cache (one byte per value, per-tensor scale only), and the fp16 copy written by
-// the repack pass (values already dequantized; no conversion at tile load).
-constexpr int kFmtNvfp4 = 0;
-constexpr int kFmtFp8 = 1;
-constexpr int kFmtF16 = 2;
-
 template <int NW, int FMT>
 struct TileRegs {
   static constexpr int kItems = 512 / (64 * NW);  // 32-value chunks per thread per tile
@@ -120,12 +113,6 @@ __device__ __forceinline__ int opaque_vzero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
   return z;
-}
-
-// Four E4M3FN bytes -> four fp16 values (two words), exact.
-__device__ __forceinline__ void fp8x4_to_f16(uint32_t w, uint32_t out[2]) {
-  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
 // Dequantize the loaded chunks to fp16 (exact) and write them to an LDS tile buffer.  The K / V
