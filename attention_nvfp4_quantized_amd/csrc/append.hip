@@ -98,8 +98,9 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
   const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane >> 2);
   const int pair = lane & 3;  // blocks 2 * pair, 2 * pair + 1
   if (t >= p.num_tokens) return;
+  // The slot only decides whether the results are stored: the input loads and the arithmetic
+  // do not wait for it (an early exit would make every load wait behind the slot load).
   const int64_t slot = p.slots[t];
-  if (slot < 0) return;
 
   const uint16_t* src = (which == 0 ? p.k + t * p.k_stride : p.v + t * p.v_stride) +
                         (int64_t)h * kHeadDim + 32 * pair;
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(256) void nvfp4_append_kernel(AppendParams p) {
   const uint32_t sa = quantize_block<UNIT_G, FP16_IN>(wa, g, pa);
   const uint32_t sb = quantize_block<UNIT_G, FP16_IN>(wb, g, pb);
 
+  if (slot < 0) return;
   const int64_t page = slot >> 4;
   const int64_t row = (page * p.num_kv_heads + h) * kPageSize + (slot & 15);
   uint8_t* data = (which == 0 ? p.k_data : p.v_data) + row * kRowBytes + 16 * pair;
@@ -156,8 +158,9 @@ __global__ __launch_bounds__(256) void fp8_append_kernel(AppendParams p) {
   const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane >> 2);
   const int qq = lane & 3;  // values 32 qq .. 32 qq + 31
   if (t >= p.num_tokens) return;
+  // The slot only decides whether the results are stored: the input loads and the arithmetic
+  // do not wait for it (an early exit would make every load wait behind the slot load).
   const int64_t slot = p.slots[t];
-  if (slot < 0) return;
 
   const uint16_t* src = (which == 0 ? p.k + t * p.k_stride : p.v + t * p.v_stride) +
                         (int64_t)h * kHeadDim + 32 * qq;
@@ -171,6 +174,7 @@ __global__ __launch_bounds__(256) void fp8_append_kernel(AppendParams p) {
     o[2 * i] = fp8_encode4<UNIT_G, FP16_IN>(in[i][0], in[i][1], g);
     o[2 * i + 1] = fp8_encode4<UNIT_G, FP16_IN>(in[i][2], in[i][3], g);
   }
+  if (slot < 0) return;
   const int64_t row = ((slot >> 4) * p.num_kv_heads + h) * kPageSize + (slot & 15);
   uint8_t* data = (which == 0 ? p.k_data : p.v_data) + row * kHeadDim + 32 * qq;
   *(u32x4*)data = u32x4{o[0], o[1], o[2], o[3]};

@@ -129,3 +129,16 @@ def test_fp8_decode_parity_full_size_sampled_sequences():
     refs = run.oracle((0, 63), sampled)
     for t in (0, 63):
         assert_attention_close(run.out[t], refs[t], f"fp8 decode step {t}")
+
+
+def test_fp8_append_skipped_slots_and_global_scales():
+    """Tokens with slot < 0 are not written (their rows stay zero), under non-unit scales."""
+    say("[fp8 append] k_global 1.5, v_global 0.75, some slots < 0")
+    pc = _case([5, 9], [70, 37], 8, 2, seed=3103)
+    slots = pc.slot_mapping.copy()
+    slots[[3, 40, 71, 106]] = -1
+    pc.slot_mapping = slots
+    g = GpuPrefillCase(pc, k_global=1.5, v_global=0.75, kv_format="fp8")
+    g.append()
+    torch.cuda.synchronize()
+    assert_cache_equal(g.cache_host(), oracle_cache(pc, k_global=1.5, v_global=0.75, kv_format="fp8"))
