@@ -70,8 +70,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int kDecodeChunkMin = 512;   // keys per decode slice, lower bound
 constexpr int kDecodeChunkMax = 8192;  // keys per decode slice, upper bound
 
-// Waves per prefill workgroup: 8 when the query tile is long enough, else the fewest 32-column
-// waves that hold every (row, head) column of the longest sequence.
+// Column wavefronts per prefill workgroup: 8 when the query tile is long enough, else the fewest
+// 32-column wavefronts that hold every (row, head) column of the longest sequence (2 selects the
+// key-split kernel, which runs two more wavefronts on the other half of each tile's keys).
 int prefill_waves(int max_q_len, int group) {
   const long cols = (long)max_q_len * group;
   if (cols >= 256) return 8;

@@ -393,7 +393,9 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const P
 }
 
 // ---- narrow kernel: NW wavefronts of 32 columns, two LDS buffers ---------------------------
-// Used for short query tiles (few columns), where the split-KV grid supplies the parallelism.
+// Used for short query tiles (few columns), where the split-KV grid supplies the parallelism:
+// NW = 4 (65..128 columns) and NW = 1 (up to 32, NVFP4 only); 33..64 columns go to the key-split
+// kernel below.
 template <int NW, int FMT>
 __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
@@ -459,6 +461,179 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
     if (kt3 + 1 < w.t_end) NVFP4KV_NARROW_STEP(kt3 + 1, r2)
 #undef NVFP4KV_NARROW_STEP
   }
+  prefill_epilogue(p, w, c, acc_o, m_used, l_part);
+}
+
+// ---- key-split kernel: 2 column wavefronts x 2 key halves -----------------------------------
+// For query tiles of at most 64 columns (short queries over long caches).  Four wavefronts load
+// and dequantize every tile together; wavefront w covers column block w & 1 and keys
+// 32 (w >> 1) .. 32 (w >> 1) + 31 of each tile, so each wavefront's per-tile chain (scores,
+// softmax, PV) is half as long and two of them share each SIMD.  The two key halves of a column
+// block are merged in LDS at the end (log-sum-exp of the two partial states).
+
+// S^T for the 32 keys of one tile half (K rows 32 half .. 32 half + 31 of the tile in `buf`).
+__device__ __forceinline__ void half_scores(const char* buf, int lane, int half,
+                                            const f16x8 (&qf)[8], f32x16& s) {
+  const char* kb = buf + (32 * half + (lane & 31)) * kKStride + 16 * (lane >> 5);
+  s = f32x16{};
+  f16x8 a[2];
+  a[0] = *(const f16x8*)(kb);
+  a[1] = *(const f16x8*)(kb + 32);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    s = mfma32h(a[t & 1], qf[t], s);
+    if (t + 2 < 8) a[t & 1] = *(const f16x8*)(kb + 32 * (t + 2));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Keys of the half starting at kh past the column's limit -> -inf.
+__device__ __forceinline__ void half_mask(f32x16& s, int kh, int lim, int h32) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (kh + 8 * (j >> 2) + 4 * h32 + (j & 3) > lim) s[j] = kNegInf;
+}
+
+__device__ __forceinline__ void half_max_rescale(const f32x16& s, float cs, float& m_used,
+                                                 float& l_part, f32x16 (&acc_o)[4]) {
+  float m = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int j = 2; j < 16; j += 2) m = fmaxf(fmaxf(m, s[j]), s[j + 1]);
+  const float mx = pair32_max(m) * cs;
+  if (wave_any(mx > m_used + 8.0f)) {
+    const float m_new = fmaxf(m_used, mx);
+    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_used - m_new);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
+    l_part *= alpha;
+    m_used = m_new;
+  }
+}
+
+__device__ __forceinline__ void half_probs(const f32x16& s, float cs, float m_used,
+                                           f16x8 (&pb)[2], float& l_part) {
+  const float mref = (m_used == kNegInf) ? 0.0f : m_used;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const f16x2 a = pack_f16x2_rtz(fast_exp2(fmaf(s[j], cs, -mref)), fast_exp2(fmaf(s[j + 1], cs, -mref)));
+    pb[j >> 3][j & 7] = a[0];
+    pb[j >> 3][(j & 7) + 1] = a[1];
+  }
+  l_part = sum_f16x8(pb[0], l_part);
+  l_part = sum_f16x8(pb[1], l_part);
+}
+
+// O^T += V^T P^T over the 32 keys of one half (key blocks u = 2 half, 2 half + 1 of the tile).
+__device__ __forceinline__ void half_pv(const char* buf, int lane, int half, const f16x8 (&pb)[2],
+                                       f32x16 (&acc_o)[4]) {
+  const int h32 = lane >> 5, g16 = lane >> 4, t16 = lane & 15;
+  const int k4 = (t16 >> 2) & 3;
+  const int slot_lo = 2 * (g16 & 1) + ((t16 & 3) >> 1);
+  const char* vb = buf + kKTileBytes + (4 * h32 + (t16 >> 2)) * kVStride +
+                   16 * (slot_lo ^ k4) + 8 * (t16 & 1);
+#pragma unroll
+  for (int uu = 0; uu < 2; ++uu) {
+    const int u = 2 * half + uu;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const char* pa = vb + 16 * u * kVStride + 64 * (db ^ k4);
+      const i16x4 lo = lds_read_tr16(pa);
+      const i16x4 hi = lds_read_tr16(pa + 8 * kVStride);
+      const f16x8 a = __builtin_bit_cast(
+          f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_o[db] = mfma32h(a, pb[uu], acc_o[db]);
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void nvfp4_prefill_ksplit_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+  PrefillItem w;
+  if (!prefill_item(p, 64, w)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int half = wave >> 1;
+  const PrefillCols c = prefill_cols(p, w, wave & 1, lane);
+  f16x8 qf[8];
+  const float cs = load_q(p, w, c, qf);
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
+  float m_used = kNegInf;
+  float l_part = 0.0f;
+  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
+
+  if (w.t_begin < w.t_end) {
+    const int vzero = opaque_vzero();
+    const int t_last = w.t_end - 1;
+    const int t0 = w.t_begin;
+    TileRegs<4, FMT> r0, r1, r2;
+    fetch_pages<4, FMT>(bt_row, w.kv_len, t0, vzero, r0);
+    load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 3, t_last), vzero, r0);
+    fetch_pages<4, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
+    load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 4, t_last), vzero, r1);
+    fetch_pages<4, FMT>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
+    load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 5, t_last), vzero, r2);
+    store_tile<4, FMT>(smem, r0);
+    load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 6, t_last), vzero, r0);
+    __syncthreads();
+#define NVFP4KV_KSPLIT_STEP(KT, R)                                                                 \
+  {                                                                                                \
+    const int kt = (KT);                                                                           \
+    char* buf = smem + ((kt - t0) & 1) * kBufBytes;                                                \
+    const int kh = kt * kTileKeys + 32 * half;                                                     \
+    if (kh <= c.wlim_max) {                                                                        \
+      f32x16 sh;                                                                                   \
+      half_scores(buf, lane, half, qf, sh);                                                        \
+      if (kh + 31 > c.wlim_min) half_mask(sh, kh, c.lim, c.h32);                                   \
+      half_max_rescale(sh, cs, m_used, l_part, acc_o);                                             \
+      f16x8 pb[2];                                                                                 \
+      half_probs(sh, cs, m_used, pb, l_part);                                                      \
+      half_pv(buf, lane, half, pb, acc_o);                                                         \
+    }                                                                                              \
+    store_tile<4, FMT>(smem + ((kt + 1 - t0) & 1) * kBufBytes, R);                                 \
+    load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 7, t_last), vzero, R); \
+    __syncthreads();                                                                               \
+  }
+    int kt3 = t0;
+    for (; kt3 + 2 < w.t_end; kt3 += 3) {
+      NVFP4KV_KSPLIT_STEP(kt3, r1)
+      NVFP4KV_KSPLIT_STEP(kt3 + 1, r2)
+      NVFP4KV_KSPLIT_STEP(kt3 + 2, r0)
+    }
+    if (kt3 < w.t_end) NVFP4KV_KSPLIT_STEP(kt3, r1)
+    if (kt3 + 1 < w.t_end) NVFP4KV_KSPLIT_STEP(kt3 + 1, r2)
+#undef NVFP4KV_KSPLIT_STEP
+  }
+
+  // merge the two key halves of each column block: half 1 hands its state over through LDS
+  // (16 KB of partial O and 512 B of (m, l) per column wavefront, inside the first tile buffer)
+  __syncthreads();
+  float* xo = (float*)smem + (wave & 1) * (64 * 64 + 2 * 64);
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xo[(16 * i + j) * 64 + lane] = acc_o[i][j];
+    xo[64 * 64 + lane] = m_used;
+    xo[64 * 64 + 64 + lane] = l_part;
+  }
+  __syncthreads();
+  if (half == 1) return;
+  const float m1 = xo[64 * 64 + lane];
+  const float l1 = xo[64 * 64 + 64 + lane];
+  const float M = fmaxf(m_used, m1);
+  const float a0 = (m_used == kNegInf) ? 0.0f : fast_exp2(m_used - M);
+  const float a1 = (m1 == kNegInf) ? 0.0f : fast_exp2(m1 - M);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc_o[i][j] = acc_o[i][j] * a0 + xo[(16 * i + j) * 64 + lane] * a1;
+  l_part = l_part * a0 + l1 * a1;
+  m_used = M;
   prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
 
@@ -588,7 +763,9 @@ hipError_t launch_prefill_fmt(const PrefillParams& p, int waves, hipStream_t str
   switch (waves) {
     case 8: hipLaunchKernelGGL(nvfp4_prefill_staggered_kernel<FMT>, grid, dim3(512), 0, stream, p); break;
     case 4: hipLaunchKernelGGL((nvfp4_prefill_kernel<4, FMT>), grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((nvfp4_prefill_kernel<2, FMT>), grid, dim3(128), 0, stream, p); break;
+    case 2:  // 33..64 columns: two column wavefronts, each tile's keys split between two more
+      hipLaunchKernelGGL(nvfp4_prefill_ksplit_kernel<FMT>, grid, dim3(256), 0, stream, p);
+      break;
     case 1:  // NVFP4 only: the host gives the wider formats two waves
       if constexpr (FMT != kFmtNvfp4) return hipErrorInvalidValue;
       else hipLaunchKernelGGL((nvfp4_prefill_kernel<1, FMT>), grid, dim3(64), 0, stream, p);
