@@ -235,11 +235,14 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
   float cs;
   {
     const uint16_t* qp = p.q + ((int64_t)b * Hq + hk * G + (colv ? col : 0)) * kHeadDim + 32 * q4;
+    // A padding lane reads column 0 (always present) and zeroes it: no branch between the loads.
     u32x4 raw[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) raw[ks] = *(const u32x4*)(qp + 8 * ks);
     float amax = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      raw[ks] = colv ? *(const u32x4*)(qp + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
+      if (!colv) raw[ks] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[ks][i] << 16)),

@@ -327,11 +327,15 @@ __device__ __forceinline__ float load_q(const PrefillParams& p, const PrefillIte
                                         const PrefillCols& c, f16x8 (&qf)[8]) {
   const uint16_t* qp = p.q + ((int64_t)(w.q_start + (c.valid ? c.pos : 0)) * p.num_qo_heads + c.head) *
                                  kHeadDim + 8 * c.h32;
+  // A padding lane reads the item's first row (it exists: an item starts inside its sequence)
+  // and zeroes what it read, so the eight loads issue together with no branch between them.
   u32x4 raw[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) raw[t] = *(const u32x4*)(qp + 16 * t);
   float amax = 0.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    raw[t] = c.valid ? *(const u32x4*)(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+    if (!c.valid) raw[t] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, raw[t][i] << 16)),
