@@ -256,6 +256,10 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
                 cache->num_kv_heads);
   const int g = num_qo_heads / cache->num_kv_heads;
   if (!group_ok(g)) return fail(NVFP4KV_EUNSUPPORTED, "query group size %d unsupported", g);
+  // output rows (token, head) are indexed in 32 bits, with room for the merge grid's rounding
+  if ((long)total_q * num_qo_heads > (1L << 30))
+    return fail(NVFP4KV_EINVAL, "total_q x num_qo_heads = %ld rows: too large for one launch",
+                (long)total_q * num_qo_heads);
   if (block_table_stride < (max_kv_len + 15) / 16)
     return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
                 block_table_stride, max_kv_len);
@@ -354,6 +358,9 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
                 cache->num_kv_heads);
   const int g = num_qo_heads / cache->num_kv_heads;
   if (g > 16) return fail(NVFP4KV_EUNSUPPORTED, "decode supports query groups of at most 16 (got %d)", g);
+  if ((long)batch * num_qo_heads > (1L << 30))
+    return fail(NVFP4KV_EINVAL, "batch x num_qo_heads = %ld rows: too large for one launch",
+                (long)batch * num_qo_heads);
   if (max_kv_len < 1) return fail(NVFP4KV_EINVAL, "max_kv_len must be >= 1");
   if (block_table_stride < (max_kv_len + 15) / 16)
     return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",

@@ -163,6 +163,7 @@ int nvfp4_kv_repack(const nvfp4kv_cache_t* src, const nvfp4kv_cache_t* dst,
  *                 whose partial results are merged (needs workspace).
  *   workspace     device scratch of at least paged_prefill_nvfp4_workspace_size(...) bytes
  *                 (may be NULL when that size is 0).
+ * total_q * num_qo_heads must not exceed 2^30 (NVFP4KV_EINVAL otherwise).
  */
 size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
                                           int32_t max_kv_len, int32_t num_qo_heads,
@@ -183,6 +184,7 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
  *   q        bf16 [batch][num_qo_heads][head_dim]; query b sees all kv_lens[b] keys.
  *   out      [batch][num_qo_heads][head_dim] bf16 or float32; lse as for prefill.
  *   num_splits  0 = automatic, else the number of key-range splits per (sequence, KV head).
+ * The query group size must be <= 16 and batch * num_qo_heads <= 2^30.
  */
 size_t paged_decode_nvfp4_workspace_size(int32_t batch, int32_t max_kv_len, int32_t num_qo_heads,
                                          int32_t num_kv_heads, int32_t head_dim,

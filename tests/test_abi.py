@@ -110,6 +110,7 @@ def test_prefill_argument_checks():
     assert _prefill(lib, d, q=None) == -1
     assert _prefill(lib, d, q=8) == -1 and "aligned" in _err()
     assert _prefill(lib, _desc(head_dim=96)) == -2
+    assert _prefill(lib, d, total_q=1 << 26) == -1 and "too large" in _err()  # 2^31 output rows
     assert _prefill(lib, d, total_q=0) == 0  # empty problem: no launch
     assert _prefill(lib, d, batch=0) == 0
 
@@ -139,6 +140,7 @@ def test_decode_argument_checks():
     assert dec(ws=None) == -3
     assert dec(wsb=100) == -3
     assert dec(max_kv=0) == -1
+    assert dec(batch=1 << 26) == -1 and "too large" in _err()  # 2^31 output rows
     assert dec(batch=0) == 0
     need = A.decode_workspace_size(64, 32768, 32, 8, num_splits=8)
     assert need == 8 * 64 * 32 * 129 * 4
