@@ -67,6 +67,10 @@ int check_not_f16(const nvfp4kv_cache_t* c, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workspace of the split paths, per (split, output row): the fp16 partial (128 values), then,
+// after all partials, its float32 log-sum-exp.
+constexpr size_t kPartRowBytes = 128 * sizeof(uint16_t) + sizeof(float);
+
 constexpr int kDecodeChunkMin = 512;   // keys per decode slice, lower bound
 constexpr int kDecodeChunkMax = 8192;  // keys per decode slice, upper bound
 
@@ -234,7 +238,7 @@ size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_
   const int q_tiles = (max_q_len + (32 * nw / g) - 1) / (32 * nw / g);
   const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, nw, num_splits);
   if (s <= 1) return 0;
-  return (size_t)s * total_q * num_qo_heads * (head_dim + 1) * sizeof(float);
+  return (size_t)s * total_q * num_qo_heads * kPartRowBytes;
 }
 
 int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_seqlens_q,
@@ -305,13 +309,13 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
   p.out_f32 = out_dtype == NVFP4KV_OUT_F32;
   hipStream_t st = (hipStream_t)stream;
   if (s > 1) {
-    const size_t need = (size_t)s * total_q * num_qo_heads * (128 + 1) * sizeof(float);
+    const size_t need = (size_t)s * total_q * num_qo_heads * kPartRowBytes;
     if (!workspace || workspace_bytes < need)
       return fail(NVFP4KV_EWORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
-    p.part_o = (float*)workspace;
-    p.part_lse = p.part_o + (size_t)s * total_q * num_qo_heads * 128;
+    p.part_o = (uint16_t*)workspace;
+    p.part_lse = (float*)(p.part_o + (size_t)s * total_q * num_qo_heads * 128);
     p.lse = nullptr;
     p.out = nullptr;
     if (int e = check_launch(nvfp4kv::launch_prefill(p, nw, st), "prefill launch")) return e;
@@ -338,7 +342,7 @@ size_t paged_decode_nvfp4_workspace_size(int32_t batch, int32_t max_kv_len, int3
     return 0;
   int chunk = 0;
   const int s = decode_splits(batch, num_kv_heads, max_kv_len, num_splits, &chunk);
-  return (size_t)s * batch * num_qo_heads * (head_dim + 1) * sizeof(float);
+  return (size_t)s * batch * num_qo_heads * kPartRowBytes;
 }
 
 int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* kv_lens,
@@ -373,7 +377,7 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
   const int s = decode_splits(batch, cache->num_kv_heads, max_kv_len, num_splits, &chunk);
   const long items = (long)cache->num_kv_heads * batch * s;
   if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
-  const size_t need = (size_t)s * batch * num_qo_heads * (128 + 1) * sizeof(float);
+  const size_t need = (size_t)s * batch * num_qo_heads * kPartRowBytes;
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4KV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -396,8 +400,8 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
   p.num_splits = s;
   p.chunk = chunk;
   p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
-  p.part_o = (float*)workspace;
-  p.part_lse = p.part_o + (size_t)s * batch * num_qo_heads * 128;
+  p.part_o = (uint16_t*)workspace;
+  p.part_lse = (float*)(p.part_o + (size_t)s * batch * num_qo_heads * 128);
   hipStream_t st = (hipStream_t)stream;
   if (int e = check_launch(nvfp4kv::launch_decode(p, st), "decode launch")) return e;
   nvfp4kv::MergeParams m{};

@@ -344,7 +344,8 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
         o = fmaf(wt, red_o[(ww * 16 + c) * kHeadDim + d], o);
       }
     }
-    p.part_o[(prow0 + c) * kHeadDim + d] = L > 0.0f ? o / L : 0.0f;
+    // fp16, nearest-even: a weighted mean of cache values before the per-tensor V scale
+    p.part_o[(prow0 + c) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(L > 0.0f ? o / L : 0.0f));
     if (d == 0) p.part_lse[prow0 + c] = L > 0.0f ? M + __log2f(L) : kNegInf;
   }
 }

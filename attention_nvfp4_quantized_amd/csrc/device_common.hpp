@@ -131,6 +131,12 @@ __device__ __forceinline__ f16x2 pack_f16x2_rtz(float lo, float hi) {
   return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
+// Two floats -> fp16 pair, rounded to nearest even; lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float lo, float hi) {
+  const f16x2 h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // acc + the sum of the eight fp16 values of v.
 __device__ __forceinline__ float sum_f16x8(f16x8 v, float acc) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};

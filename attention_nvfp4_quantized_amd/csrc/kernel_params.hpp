@@ -65,7 +65,7 @@ struct PrefillParams {
   float* lse;             // optional [total_q][Hq] (natural log); unused in split mode
   void* out;              // [total_q][Hq][D]
   int32_t out_f32;
-  float* part_o;          // split mode: [num_splits][total_q][Hq][D]
+  uint16_t* part_o;       // split mode: fp16 [num_splits][total_q][Hq][D]
   float* part_lse;        // split mode: [num_splits][total_q][Hq] (log2 units)
   int32_t format;         // cache format: 0 NVFP4, 1 FP8 E4M3FN, 2 fp16 (repacked)
 };
@@ -84,7 +84,7 @@ struct RepackParams {
 };
 
 struct MergeParams {
-  const float* part_o;
+  const uint16_t* part_o;  // fp16 [num_splits][rows][D]
   const float* part_lse;
   int32_t num_splits;
   int32_t rows;          // total_q * Hq
@@ -110,7 +110,7 @@ struct DecodeParams {
   int32_t num_splits;
   int32_t chunk;          // keys per split (multiple of 64)
   float score_scale;
-  float* part_o;          // [num_splits][batch][Hq][D]
+  uint16_t* part_o;       // fp16 [num_splits][batch][Hq][D]
   float* part_lse;        // [num_splits][batch][Hq]
   int32_t fp8;            // FP8 E4M3FN cache (else NVFP4)
 };

@@ -357,7 +357,9 @@ __device__ __forceinline__ float load_q(const PrefillParams& p, const PrefillIte
 }
 
 // Normalise and store this lane's half of its column: O (bf16 or fp32) and the log-sum-exp,
-// or, in split mode, the slice's normalised partial and its base-2 log-sum-exp.
+// or, in split mode, the slice's normalised partial (fp16, nearest-even: before the per-tensor
+// V scale it is a weighted mean of cache values, |x| <= 6 * 448, well inside fp16's range) and
+// its base-2 log-sum-exp.
 __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const PrefillItem& w,
                                                  const PrefillCols& c, const f32x16 (&acc_o)[4],
                                                  float m_used, float l_part) {
@@ -366,9 +368,18 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const P
   const int64_t orow = (int64_t)(w.q_start + c.pos) * p.num_qo_heads + c.head;
   const bool split_mode = p.num_splits > 1;
   const float inv = l_tot > 0.0f ? (split_mode ? 1.0f : p.out_scale) / l_tot : 0.0f;
-  if (split_mode || p.out_f32) {
-    float* op = split_mode ? p.part_o + ((int64_t)w.split * p.total_q * p.num_qo_heads + orow) * kHeadDim
-                           : (float*)p.out + orow * kHeadDim;
+  if (split_mode) {
+    uint16_t* op = p.part_o + ((int64_t)w.split * p.total_q * p.num_qo_heads + orow) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * c.h32;
+        *(u32x2*)(op + d) = u32x2{pack_f16x2_rne(acc_o[db][4 * jg] * inv, acc_o[db][4 * jg + 1] * inv),
+                                  pack_f16x2_rne(acc_o[db][4 * jg + 2] * inv, acc_o[db][4 * jg + 3] * inv)};
+      }
+  } else if (p.out_f32) {
+    float* op = (float*)p.out + orow * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -732,8 +743,8 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
   prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
 
-// Log-sum-exp merge of split partials: one wavefront per (query row, head); lane l owns
-// head-dim values 2l and 2l+1.  The lanes read the slices' log-sum-exps in parallel and take
+// Log-sum-exp merge of split partials (fp16 values, float32 log-sum-exps): one wavefront per
+// (query row, head); lane l owns head-dim values 2l and 2l+1.  The lanes read the slices' log-sum-exps in parallel and take
 // their maximum across the wavefront; the partials are then read eight slices at a time with
 // the eight loads issued together (a partial of an empty slice is read but not used: it is not
 // written), and accumulated in slice order.
@@ -750,20 +761,20 @@ __global__ __launch_bounds__(256) void nvfp4_merge_kernel(MergeParams p) {
   if (mx != kNegInf) {
     for (int s0 = 0; s0 < S; s0 += 8) {
       float ls[8];
-      f32x2 v[8];
+      f16x2 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t r = (int64_t)min(s0 + j, S - 1) * p.rows + row;
         ls[j] = p.part_lse[r];
-        v[j] = *(const f32x2*)(p.part_o + r * kHeadDim + 2 * lane);
+        v[j] = *(const f16x2*)(p.part_o + r * kHeadDim + 2 * lane);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bool use = s0 + j < S && ls[j] != kNegInf;
         const float wgt = use ? fast_exp2(ls[j] - mx) : 0.0f;
         wsum += wgt;
-        o0 = use ? fmaf(wgt, v[j][0], o0) : o0;
-        o1 = use ? fmaf(wgt, v[j][1], o1) : o1;
+        o0 = use ? fmaf(wgt, (float)v[j][0], o0) : o0;
+        o1 = use ? fmaf(wgt, (float)v[j][1], o1) : o1;
       }
     }
   }

@@ -119,7 +119,7 @@ def test_prefill_split_needs_workspace():
     lib = load_library()
     d = _desc()
     need = A.prefill_workspace_size(1, 16, 16, 128, 32, 8, num_splits=4)
-    assert need == 4 * 16 * 32 * 129 * 4
+    assert need == 4 * 16 * 32 * (128 * 2 + 4)  # fp16 partial + float32 log-sum-exp per row
     assert _prefill(lib, d, splits=4) == -3 and str(need) in _err()
     assert _prefill(lib, d, splits=4, ws=16, wsb=need - 1) == -3
 
@@ -143,7 +143,7 @@ def test_decode_argument_checks():
     assert dec(batch=1 << 26) == -1 and "too large" in _err()  # 2^31 output rows
     assert dec(batch=0) == 0
     need = A.decode_workspace_size(64, 32768, 32, 8, num_splits=8)
-    assert need == 8 * 64 * 32 * 129 * 4
+    assert need == 8 * 64 * 32 * (128 * 2 + 4)
 
 
 def test_workspace_sizes_follow_split_policy():
