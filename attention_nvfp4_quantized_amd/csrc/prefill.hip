@@ -279,9 +279,9 @@ __device__ __forceinline__ bool prefill_item(const PrefillParams& p, int cols, P
   const int rows_per_tile = cols / p.group;
   w.q_start = p.cu_q[w.b];
   w.q_len = p.cu_q[w.b + 1] - w.q_start;
+  w.kv_len = p.kv_lens[w.b];  // read with cu_q, not after the test below
   w.pos0 = qt * rows_per_tile;
   if (w.pos0 >= w.q_len) return false;
-  w.kv_len = p.kv_lens[w.b];
   w.pos_last = min(w.q_len, w.pos0 + rows_per_tile) - 1;
   w.shift = p.causal ? w.kv_len - w.q_len : 0;  // row i sees keys <= i + shift
   const int lim_tile = p.causal ? w.shift + w.pos_last : w.kv_len - 1;
@@ -418,6 +418,22 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
   if (!prefill_item(p, 32 * NW, w)) return;
   const int lane = threadIdx.x & 63;
   const PrefillCols c = prefill_cols(p, w, uniform(threadIdx.x >> 6), lane);
+  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
+  const bool has_tiles = w.t_begin < w.t_end;
+  const int vzero = opaque_vzero();
+  const int t_last = w.t_end - 1;
+  const int t0 = w.t_begin;
+  // Three register sets in rotation: the packed loads of tile kt+4 are issued while tile kt is
+  // consumed, so each tile's loads have three tiles of compute to arrive (these short-query
+  // shapes are bound by memory latency).  The first three tiles' page ids are fetched before
+  // the Q loads and their chunks loaded together.  Tile indices are clamped at t_last; writes
+  // past the last tile land in a buffer that is not read again.
+  TileRegs<NW, FMT> r0, r1, r2;
+  if (has_tiles) {
+    fetch_pages<NW, FMT>(bt_row, w.kv_len, t0, vzero, r0);
+    fetch_pages<NW, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
+    fetch_pages<NW, FMT>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
+  }
   f16x8 qf[8];
   const float cs = load_q(p, w, c, qf);
 
@@ -426,22 +442,10 @@ __global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p)
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
   float m_used = kNegInf;
   float l_part = 0.0f;
-  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
-  if (w.t_begin < w.t_end) {
-    // Three register sets in rotation: the packed loads of tile kt+4 are issued while tile kt is
-    // consumed, so each tile's loads have three tiles of compute to arrive (these short-query
-    // shapes are bound by memory latency).  Tile indices are clamped at t_last; writes past the
-    // last tile land in a buffer that is not read again.
-    const int vzero = opaque_vzero();
-    const int t_last = w.t_end - 1;
-    const int t0 = w.t_begin;
-    TileRegs<NW, FMT> r0, r1, r2;
-    fetch_pages<NW, FMT>(bt_row, w.kv_len, t0, vzero, r0);
+  if (has_tiles) {
     load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 3, t_last), vzero, r0);
-    fetch_pages<NW, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
     load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 4, t_last), vzero, r1);
-    fetch_pages<NW, FMT>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
     load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 5, t_last), vzero, r2);
     store_tile<NW, FMT>(smem, r0);
     load_tile<NW, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 6, t_last), vzero, r0);
@@ -571,6 +575,18 @@ __global__ __launch_bounds__(256, 2) void nvfp4_prefill_ksplit_kernel(PrefillPar
   const int wave = uniform(threadIdx.x >> 6);
   const int half = wave >> 1;
   const PrefillCols c = prefill_cols(p, w, wave & 1, lane);
+  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
+  const bool has_tiles = w.t_begin < w.t_end;
+  const int vzero = opaque_vzero();
+  const int t_last = w.t_end - 1;
+  const int t0 = w.t_begin;
+  // the first three tiles' page ids go out before the Q loads (as in the narrow kernel)
+  TileRegs<4, FMT> r0, r1, r2;
+  if (has_tiles) {
+    fetch_pages<4, FMT>(bt_row, w.kv_len, t0, vzero, r0);
+    fetch_pages<4, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
+    fetch_pages<4, FMT>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
+  }
   f16x8 qf[8];
   const float cs = load_q(p, w, c, qf);
 
@@ -579,18 +595,10 @@ __global__ __launch_bounds__(256, 2) void nvfp4_prefill_ksplit_kernel(PrefillPar
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
   float m_used = kNegInf;
   float l_part = 0.0f;
-  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
-  if (w.t_begin < w.t_end) {
-    const int vzero = opaque_vzero();
-    const int t_last = w.t_end - 1;
-    const int t0 = w.t_begin;
-    TileRegs<4, FMT> r0, r1, r2;
-    fetch_pages<4, FMT>(bt_row, w.kv_len, t0, vzero, r0);
+  if (has_tiles) {
     load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 3, t_last), vzero, r0);
-    fetch_pages<4, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, r1);
     load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 4, t_last), vzero, r1);
-    fetch_pages<4, FMT>(bt_row, w.kv_len, min(t0 + 2, t_last), vzero, r2);
     load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 5, t_last), vzero, r2);
     store_tile<4, FMT>(smem, r0);
     load_tile<4, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 6, t_last), vzero, r0);
@@ -673,6 +681,20 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
   const int wave = uniform(threadIdx.x >> 6);
   const bool ahead = wave >= 4;  // group 1 scores the next tile before each barrier
   const PrefillCols c = prefill_cols(p, w, wave, lane);
+  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
+  const bool has_tiles = w.t_begin < w.t_end;
+  const int vzero = opaque_vzero();
+  const int t_last = w.t_end - 1;
+  const int t0 = w.t_begin;
+  // Two register sets take turns: the packed loads of tile kt+4 are issued while tile kt is
+  // consumed, two tiles ahead of their dequantization.  The first two tiles' page ids are
+  // fetched before the Q loads and their chunks loaded together.  Tile indices are clamped at
+  // t_last.
+  TileRegs<kStagWaves, FMT> ra, rb;
+  if (has_tiles) {
+    fetch_pages<kStagWaves, FMT>(bt_row, w.kv_len, t0, vzero, ra);
+    fetch_pages<kStagWaves, FMT>(bt_row, w.kv_len, min(t0 + 1, t_last), vzero, rb);
+  }
   f16x8 qf[8];
   const float cs = load_q(p, w, c, qf);
 
@@ -681,23 +703,14 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
   for (int i = 0; i < 4; ++i) acc_o[i] = f32x16{};
   float m_used = kNegInf;
   float l_part = 0.0f;
-  const int32_t* bt_row = p.block_table + (int64_t)w.b * p.bt_stride;
 
-  if (w.t_begin < w.t_end) {
-    // Two register sets take turns: the packed loads of tile kt+4 are issued while tile kt is
-    // consumed, two tiles ahead of their dequantization.  Tile indices are clamped at t_last.
-    const int vzero = opaque_vzero();
-    const int t_last = w.t_end - 1;
-    const int t0 = w.t_begin;
-    TileRegs<kStagWaves, FMT> ra, rb;
-    fetch_pages<kStagWaves, FMT>(bt_row, w.kv_len, t0, vzero, ra);
-    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 1, t_last), vzero, ra);
+  if (has_tiles) {
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 2, t_last), vzero, ra);
+    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 3, t_last), vzero, rb);
     store_tile<kStagWaves, FMT>(smem, ra);
-    load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 2, t_last), vzero, ra);
-    store_tile<kStagWaves, FMT>(smem + kBufBytes, ra);
+    store_tile<kStagWaves, FMT>(smem + kBufBytes, rb);
     __syncthreads();
     load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 4, t_last), vzero, ra);
-    fetch_pages<kStagWaves, FMT>(bt_row, w.kv_len, min(t0 + 3, t_last), vzero, rb);
     load_tile<kStagWaves, FMT>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 5, t_last), vzero, rb);
 
     f32x16 s0 = f32x16{}, s1 = f32x16{};
