@@ -47,7 +47,7 @@ PREFILL_KERNEL = "nvfp4_prefill_staggered_kernel<0>"  # the NVFP4 instantiation
 PREFILL_SOURCES = ["prefill.hip", "device_common.hpp", "kernel_params.hpp"]
 DECODE_KERNEL = "nvfp4_decode_kernel<0>"
 DECODE_SOURCES = ["decode.hip", "device_common.hpp", "kernel_params.hpp"]
-CPU_ROWS = 1024  # query rows of the 16K prefill in the oracle's timed sample
+CPU_TARGET_S = 12.0  # seconds of oracle work the timed CPU sample aims at
 
 
 def prefill_flops(q_lens, kv_lens, hq, d=128) -> float:
@@ -221,7 +221,7 @@ def decode_result(w, fmt, lens_np, ev, loop_s):
     return out
 
 
-def run_repack_prefill(name, torch, A, reps=20, warmup=5):
+def run_repack_prefill(name, torch, A, reps=20):
     """Dequantize-ahead repack on a short-query workload: median µs of the repack pass (every
     page the batch reads, NVFP4 -> fp16 copy), of the prefill over the copy, and of both
     together, with a 512 MB buffer written before each call (cold caches), against the stock
@@ -245,10 +245,12 @@ def run_repack_prefill(name, torch, A, reps=20, warmup=5):
     def prefill(c):
         A.prefill(c, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out, workspace=ws)
 
-    for _ in range(warmup):
+    def both():
         A.repack(cache, dst, bt, kv, pc.max_kv_len)
         prefill(dst)
         prefill(cache)
+
+    warm_up(both, torch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
     for i in range(reps):
         flush.zero_()
@@ -272,6 +274,20 @@ def run_repack_prefill(name, torch, A, reps=20, warmup=5):
 _CASES = {}
 
 
+def warm_up(fn, torch, min_calls=20, min_seconds=0.25):
+    """Untimed calls of `fn` until at least `min_calls` have run and at least `min_seconds` of
+    GPU time have passed (the shader clock ramps over the first launches after an idle spell,
+    such as the host-side input generation that precedes each leg)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or time.perf_counter() - t0 < min_seconds:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def prefill_case(name):
     """Seeded host inputs of a prefill workload, generated once per run."""
     if name not in _CASES:
@@ -279,7 +295,7 @@ def prefill_case(name):
     return _CASES[name]
 
 
-def run_full_prefill(name, torch, A, reps=8, warmup=4, kv_format="nvfp4"):
+def run_full_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
     """Kernel time of the append and the causal prefill of a full-length single request (the
     pages' benchmark matrix asks for full 8K and 32K prefill next to the tail shapes)."""
     pc = prefill_case(name)
@@ -293,13 +309,17 @@ def run_full_prefill(name, torch, A, reps=8, warmup=4, kv_format="nvfp4"):
     bt = torch.from_numpy(pc.layout.block_table).cuda()
     out = torch.empty((pc.total_q, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-    for i in range(warmup + reps):
-        e = ev[i - warmup] if i >= warmup else None
+
+    def step(e=None):
         if e: e[0].record()
         A.append(cache, k, v, slots)
         if e: e[1].record()
         A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out)
         if e: e[2].record()
+
+    warm_up(step, torch)
+    for e in ev:
+        step(e)
     torch.cuda.synchronize()
     pre = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     app = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
@@ -310,7 +330,7 @@ def run_full_prefill(name, torch, A, reps=8, warmup=4, kv_format="nvfp4"):
             "append_us": round(app * 1e3, 2), "flop_per_call": flops}
 
 
-def run_short_prefill(name, torch, A, reps=20, warmup=5, kv_format="nvfp4"):
+def run_short_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
     """Prefill-only timing of a short-query workload (tail128: 4 x 128 queries over 2,048 keys;
     tail16: 8 x 16 queries over 16,384 keys): median µs per call with a 512 MB buffer written
     between calls (flushing L2 and MALL, so the packed cache comes from HBM) and warm
@@ -334,8 +354,7 @@ def run_short_prefill(name, torch, A, reps=20, warmup=5, kv_format="nvfp4"):
         A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out,
                   workspace=ws)
 
-    for _ in range(warmup):
-        call()
+    warm_up(call, torch)
     times = {}
     for mode in ("flushed", "warm"):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
@@ -358,11 +377,12 @@ def run_short_prefill(name, torch, A, reps=20, warmup=5, kv_format="nvfp4"):
             "flop_per_call": flops, "bytes_per_call": int(nbytes)}
 
 
-def run_cpu_baseline(pc):
-    """The oracle, untuned, on a bounded sample of the 16K prefill: all 32 heads of CPU_ROWS
-    query rows spread evenly over the sequence (their visible keys included; about ten seconds
-    of float64 work on 16 host cores), after the oracle's append of all 16,384 tokens (timed
-    separately)."""
+def run_cpu_baseline(pc, target_s=CPU_TARGET_S):
+    """The oracle, untuned, on a bounded sample of the 16K prefill: all 32 heads of query rows
+    spread evenly over the sequence (their visible keys included), after the oracle's append of
+    all 16,384 tokens (timed separately).  Two short untimed calls (32 and 96 rows) give the
+    host's fixed cost per call and time per row; the timed call then takes as many rows as fill
+    about `target_s` seconds, so the sample is about that long on any host."""
     from oracle import attention as oattn
     from oracle import cache as ocache
     try:
@@ -375,11 +395,22 @@ def run_cpu_baseline(pc):
     oc = ocache.PagedCache(pc.layout.num_pages, w.num_kv_heads)
     oc.append(pc.k_bits, pc.v_bits, pc.slot_mapping)
     t_append = time.perf_counter() - t0
-    rows = np.linspace(0, pc.total_q - 1, CPU_ROWS).round().astype(np.int64)
-    t0 = time.perf_counter()
-    oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table, w.sm_scale,
-                  rows=rows)
-    t_pre = time.perf_counter() - t0
+
+    def spread(n):
+        return np.unique(np.linspace(0, pc.total_q - 1, n).round().astype(np.int64))
+
+    def run(rows):
+        t = time.perf_counter()
+        oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
+                      w.sm_scale, rows=rows)
+        return time.perf_counter() - t
+
+    t32, t96 = run(spread(32)), run(spread(96))
+    per_row = max((t96 - t32) / 64, 1e-6)
+    fixed = max(t32 - 32 * per_row, 0.0)
+    n = int(np.clip((target_s - fixed) / per_row, 96, pc.total_q))
+    rows = spread(n)
+    t_pre = run(rows)
     flops = 4.0 * 128 * w.num_qo_heads * float((rows + 1).sum())
     cores = len(os.sched_getaffinity(0))
     return {"value": round(flops / t_pre / 1e12, 6), "unit": "TFLOP/s",
@@ -387,8 +418,8 @@ def run_cpu_baseline(pc):
             "sample": "oracle float64 prefill of %d evenly spaced query rows x 32 heads of the "
                       "16K causal prefill (%.3g algorithmic FLOP, %.1f s), after the oracle's "
                       "append of all 16,384 tokens (%.1f s, not in value)"
-                      % (CPU_ROWS, flops, t_pre, t_append),
-            "seconds": round(t_pre + t_append, 2)}
+                      % (len(rows), flops, t_pre, t_append),
+            "rows": int(len(rows)), "seconds": round(t_pre + t_append, 2)}
 
 
 def fp8_summary(line, fp8):
