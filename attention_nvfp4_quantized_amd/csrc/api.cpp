@@ -88,7 +88,7 @@ int prefill_waves(int max_q_len, int group) {
 // Key slices per prefill work item.  Slicing buys parallelism when there are fewer work items
 // than the GPU holds at once (256 CUs x workgroups per CU: one 8-wave workgroup, whose three
 // tile buffers fill most of the LDS, or two narrow ones), but every extra slice writes and
-// re-reads an fp32 partial of the whole output; so slice only up to that occupancy, and keep at
+// re-reads an fp16 partial of the whole output; so slice only up to that occupancy, and keep at
 // least 8 tiles (512 keys) per slice.
 int prefill_splits(int batch, int q_tiles, int num_kv_heads, int max_kv_len, int nw, int requested) {
   if (requested > 0) return requested;
