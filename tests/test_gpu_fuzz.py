@@ -15,8 +15,8 @@ from oracle import attention as oattn
 
 pytestmark = pytest.mark.gpu
 
-N_PREFILL = 24
-N_DECODE = 12
+N_PREFILL = 64
+N_DECODE = 32
 
 
 def _prefill_config(i):
