@@ -20,8 +20,9 @@
 //  * The four wavefronts are combined in LDS; one partial (o, log2-sum-exp) per (sequence, query
 //    head, slice) goes to the workspace, and a merge kernel reduces the slices.
 //  * The workgroup -> (KV head, sequence, slice) map keeps each KV head on one XCD.
-//  * Only a wavefront's last group of four steps can hold tokens past its range; the groups
-//    before it run without any per-token range selects or score masks.
+//  * Loads run in a ring of register sets (two steps ahead for NVFP4, four for the FP8 control);
+//    only a wavefront's last group of ring-depth steps can hold tokens past its range, and the
+//    groups before it run without any per-token range selects or score masks.
 //  * The same kernel reads the FP8 (E4M3FN) control cache (FMT = 1): 32 bytes per lane and
 //    token, one conversion per pair of values and no block scales.
 #include "device_common.hpp"
@@ -198,8 +199,24 @@ __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Register sets of loads in rotation (kRing - 1 steps in flight while one is consumed) and
+// workgroups per CU for each cache format.  NVFP4: three sets at three workgroups, i.e. three
+// wavefronts per SIMD (158 registers).  FP8, whose sets are twice the size: five sets at two
+// workgroups (238 registers).  Measured against deeper rings and other occupancies, these were
+// the fastest of the shapes that do not spill.
 template <int FMT>
-__global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
+struct DecodeShape;
+template <>
+struct DecodeShape<kFmtNvfp4> {
+  static constexpr int kRing = 3, kBlocks = 3;
+};
+template <>
+struct DecodeShape<kFmtFp8> {
+  static constexpr int kRing = 5, kBlocks = 2;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256, DecodeShape<FMT>::kBlocks) void nvfp4_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kDecWaves * kDecStageBytes];
   __shared__ float red_m[kDecWaves][16];
   __shared__ float red_l[kDecWaves][16];
@@ -285,35 +302,33 @@ __global__ __launch_bounds__(256) void nvfp4_decode_kernel(DecodeParams p) {
     int pt0, pt1;
     asm volatile("v_mov_b32 %0, %1" : "=v"(pt0) : "v"(pt0_ld));
     asm volatile("v_mov_b32 %0, %1" : "=v"(pt1) : "v"(pt1_ld));
-    // four register sets in rotation: the loads of three 32-token steps are in flight while
-    // the fourth is consumed
-    DecodeRegs<FMT> r0, r1, r2, r3;
-    decode_load(p, hk, wk0, wk1, pt0, pt1, wk0, lane, r0);
-    decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + kDecStep, lane, r1);
-    decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + 2 * kDecStep, lane, r2);
-#define NVFP4KV_DECODE_STAGE(CUR, NXT, OFF, FULL)                                    \
-  {                                                                                  \
-    decode_load(p, hk, wk0, wk1, pt0, pt1, k + (OFF) + 3 * kDecStep, lane, NXT);    \
-    __builtin_amdgcn_sched_barrier(0);                                               \
-    decode_step<FMT, FULL>(CUR, k + (OFF), wk1, lane, qf, cs, stage, st);            \
-    __builtin_amdgcn_sched_barrier(0);                                               \
-  }
-    // groups of four steps wholly inside [wk0, wk1) skip every range check; the last group
-    // masks the keys past wk1
+    // register sets in rotation: the loads of kRing - 1 32-token steps are in flight while
+    // the next one is consumed
+    constexpr int R = DecodeShape<FMT>::kRing;
+    DecodeRegs<FMT> r[R];
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) decode_load(p, hk, wk0, wk1, pt0, pt1, wk0 + i * kDecStep, lane, r[i]);
+    // groups of R steps wholly inside [wk0, wk1) skip every range check; the last group masks
+    // the keys past wk1
     int k = wk0;
-    for (; k + 4 * kDecStep <= wk1; k += 4 * kDecStep) {
-      NVFP4KV_DECODE_STAGE(r0, r3, 0, true)
-      NVFP4KV_DECODE_STAGE(r1, r0, kDecStep, true)
-      NVFP4KV_DECODE_STAGE(r2, r1, 2 * kDecStep, true)
-      NVFP4KV_DECODE_STAGE(r3, r2, 3 * kDecStep, true)
+    for (; k + R * kDecStep <= wk1; k += R * kDecStep) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        decode_load(p, hk, wk0, wk1, pt0, pt1, k + (i + R - 1) * kDecStep, lane, r[(i + R - 1) % R]);
+        __builtin_amdgcn_sched_barrier(0);
+        decode_step<FMT, true>(r[i], k + i * kDecStep, wk1, lane, qf, cs, stage, st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (k < wk1) {
-      NVFP4KV_DECODE_STAGE(r0, r3, 0, false)
-      NVFP4KV_DECODE_STAGE(r1, r0, kDecStep, false)
-      NVFP4KV_DECODE_STAGE(r2, r1, 2 * kDecStep, false)
-      NVFP4KV_DECODE_STAGE(r3, r2, 3 * kDecStep, false)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        decode_load(p, hk, wk0, wk1, pt0, pt1, k + (i + R - 1) * kDecStep, lane, r[(i + R - 1) % R]);
+        __builtin_amdgcn_sched_barrier(0);
+        decode_step<FMT, false>(r[i], k + i * kDecStep, wk1, lane, qf, cs, stage, st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-#undef NVFP4KV_DECODE_STAGE
   }
 
   // ---- combine the four wavefronts in LDS
