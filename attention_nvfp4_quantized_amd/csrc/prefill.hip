@@ -411,8 +411,11 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const P
 // Used for short query tiles (few columns), where the split-KV grid supplies the parallelism:
 // NW = 4 (65..128 columns) and NW = 1 (up to 32, NVFP4 only); 33..64 columns go to the key-split
 // kernel below.
+// The four-wave form asks for two workgroups per CU (registers capped at 256: 232 for NVFP4, 246
+// for FP8, no spills; two tile buffers each fit the LDS twice), which the host's split count
+// assumes; the fp16 (repacked) form would spill there and keeps one.
 template <int NW, int FMT>
-__global__ __launch_bounds__(64 * NW) void nvfp4_prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * NW, (NW == 4 && FMT != kFmtF16) ? 2 : 1) void nvfp4_prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
   PrefillItem w;
   if (!prefill_item(p, 32 * NW, w)) return;
