@@ -74,15 +74,15 @@ constexpr size_t kPartRowBytes = 128 * sizeof(uint16_t) + sizeof(float);
 constexpr int kDecodeChunkMin = 512;   // keys per decode slice, lower bound
 constexpr int kDecodeChunkMax = 8192;  // keys per decode slice, upper bound
 
-// Column wavefronts per prefill workgroup: 8 when the query tile is long enough, else the fewest
-// 32-column wavefronts that hold every (row, head) column of the longest sequence (2 selects the
-// key-split kernel, which runs two more wavefronts on the other half of each tile's keys).
+// Column wavefronts per prefill workgroup: 8 when the query tile is long enough (256 columns or
+// more), 4 for 65-255 columns, else 2, which selects the key-split kernel (two column wavefronts,
+// each tile's keys split between two more).  At 32 columns or fewer the second column wavefront
+// only pads, and the kernel still runs about twice as fast as one wavefront walking every key.
 int prefill_waves(int max_q_len, int group) {
   const long cols = (long)max_q_len * group;
   if (cols >= 256) return 8;
   if (cols > 64) return 4;
-  if (cols > 32) return 2;
-  return 1;
+  return 2;
 }
 
 // Key slices per prefill work item.  Slicing buys parallelism when there are fewer work items
@@ -272,11 +272,7 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
     return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
   if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
 
-  // The one-wave kernel holds three tiles of chunks in registers; the FP8 and fp16 chunks are
-  // two and four times the packed NVFP4 size and would spill there, so those formats take the
-  // two-wave kernel (a single query tile either way: the split count and workspace are the same).
-  int nw = prefill_waves(max_q_len, g);
-  if (nw == 1 && cache->kv_format != NVFP4KV_FORMAT_NVFP4) nw = 2;
+  const int nw = prefill_waves(max_q_len, g);
   const int rows = 32 * nw / g;
   const int q_tiles = (max_q_len + rows - 1) / rows;
   const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);

@@ -408,14 +408,13 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const P
 }
 
 // ---- narrow kernel: NW wavefronts of 32 columns, two LDS buffers ---------------------------
-// Used for short query tiles (few columns), where the split-KV grid supplies the parallelism:
-// NW = 4 (65..128 columns) and NW = 1 (up to 32, NVFP4 only); 33..64 columns go to the key-split
-// kernel below.
-// The four-wave form asks for two workgroups per CU (registers capped at 256: 232 for NVFP4, 246
-// for FP8, no spills; two tile buffers each fit the LDS twice), which the host's split count
-// assumes; the fp16 (repacked) form would spill there and keeps one.
+// Used for short query tiles, where the split-KV grid supplies the parallelism: NW = 4 (65..255
+// columns); up to 64 columns go to the key-split kernel below.  It asks for two workgroups per CU
+// (registers capped at 256: 232 for NVFP4, 246 for FP8, no spills; two tile buffers each fit the
+// LDS twice), which the host's split count assumes; the fp16 (repacked) form would spill there
+// and keeps one.
 template <int NW, int FMT>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && FMT != kFmtF16) ? 2 : 1) void nvfp4_prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * NW, FMT == kFmtF16 ? 1 : 2) void nvfp4_prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
   PrefillItem w;
   if (!prefill_item(p, 32 * NW, w)) return;
@@ -809,12 +808,8 @@ hipError_t launch_prefill_fmt(const PrefillParams& p, int waves, hipStream_t str
   switch (waves) {
     case 8: hipLaunchKernelGGL(nvfp4_prefill_staggered_kernel<FMT>, grid, dim3(512), 0, stream, p); break;
     case 4: hipLaunchKernelGGL((nvfp4_prefill_kernel<4, FMT>), grid, dim3(256), 0, stream, p); break;
-    case 2:  // 33..64 columns: two column wavefronts, each tile's keys split between two more
+    case 2:  // up to 64 columns: two column wavefronts, each tile's keys split between two more
       hipLaunchKernelGGL(nvfp4_prefill_ksplit_kernel<FMT>, grid, dim3(256), 0, stream, p);
-      break;
-    case 1:  // NVFP4 only: the host gives the wider formats two waves
-      if constexpr (FMT != kFmtNvfp4) return hipErrorInvalidValue;
-      else hipLaunchKernelGGL((nvfp4_prefill_kernel<1, FMT>), grid, dim3(64), 0, stream, p);
       break;
     default: return hipErrorInvalidValue;
   }
