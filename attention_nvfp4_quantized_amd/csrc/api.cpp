@@ -74,13 +74,15 @@ constexpr size_t kPartRowBytes = 128 * sizeof(uint16_t) + sizeof(float);
 constexpr int kDecodeChunkMin = 512;   // keys per decode slice, lower bound
 constexpr int kDecodeChunkMax = 8192;  // keys per decode slice, upper bound
 
-// Column wavefronts per prefill workgroup: 8 when the query tile is long enough (256 columns or
-// more), 4 for 65-255 columns, else 2, which selects the key-split kernel (two column wavefronts,
-// each tile's keys split between two more).  At 32 columns or fewer the second column wavefront
-// only pads, and the kernel still runs about twice as fast as one wavefront walking every key.
+// Column wavefronts per prefill workgroup (query columns = rows x group of the longest
+// sequence): 8 above 128 columns (the 8-wave kernel's 256-column tiles, the last one padded; from
+// 129 columns on it beats the four-wave kernel), 4 for 65-128, else 2, which selects the
+// key-split kernel (two column wavefronts, each tile's keys split between two more).  At 32
+// columns or fewer the second column wavefront only pads, and the kernel still runs about twice
+// as fast as one wavefront walking every key.
 int prefill_waves(int max_q_len, int group) {
   const long cols = (long)max_q_len * group;
-  if (cols >= 256) return 8;
+  if (cols > 128) return 8;
   if (cols > 64) return 4;
   return 2;
 }
