@@ -143,6 +143,22 @@ def test_prefill_group_sizes(hq, hkv):
     assert_attention_close(o, ref, f"G={hq // hkv}")
 
 
+@pytest.mark.parametrize("kv_format", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("q_max", [8, 9, 16, 17, 32, 33, 64, 65])
+def test_prefill_kernel_boundaries(q_max, kv_format):
+    """Query tiles on each side of the kernel choices at group size 4 (32 / 8 heads): up to 64
+    columns (16 rows) the key-split kernel, 65-128 the four-wave kernel, above 128 the 8-wave
+    kernel; the longest sequence decides, the shorter one rides in padded tiles."""
+    say(f"[prefill] kernel boundary: max q_len {q_max} ({4 * q_max} columns), {kv_format}")
+    pc = _case([q_max, max(1, q_max // 3)], [q_max + 700, q_max // 3 + 90], seed=3020 + q_max, k_out=10)
+    g = GpuPrefillCase(pc, kv_format=kv_format)
+    g.append()
+    o, lse = g.prefill(torch.float32, return_lse=True)
+    ref, ref_lse = oracle_prefill(pc, oracle_cache(pc, kv_format=kv_format))
+    assert_attention_close(o.cpu().numpy(), ref, f"q_max={q_max} {kv_format}")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
 def test_prefill_split_sweep(splits):
     say(f"[prefill] tails, num_splits={splits}")
