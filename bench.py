@@ -331,8 +331,9 @@ def run_full_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
 
 
 def run_short_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
-    """Prefill-only timing of a short-query workload (tail128: 4 x 128 queries over 2,048 keys;
-    tail16: 8 x 16 queries over 16,384 keys): median µs per call with a 512 MB buffer written
+    """Prefill-only timing of a short workload (tiny: 1 x 256 queries over 256 keys, 4 / 1 heads;
+    tail128: 4 x 128 queries over 2,048 keys; tail16: 8 x 16 queries over 16,384 keys): median µs
+    per call with a 512 MB buffer written
     between calls (flushing L2 and MALL, so the packed cache comes from HBM) and warm
     back-to-back, with algorithmic TFLOP/s and GB/s (Q + O + packed KV of every sequence)."""
     pc = prefill_case(name)
@@ -459,7 +460,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-short", action="store_true",
-                    help="skip the tail128 / tail16 prefill timings (stock and repacked)")
+                    help="skip the tiny / tail128 / tail16 prefill timings (stock; repacked for the tails)")
     ap.add_argument("--no-matrix", action="store_true", help="skip the full 8K / 32K prefill timings")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 control-cache timings")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -503,10 +504,10 @@ def main():
         if "fp8" in dec:
             fp8["decode"] = dec["fp8"]
     if not args.no_short:
-        line["short_prefill"] = [run_short_prefill(n, torch, A) for n in ("tail128", "tail16")]
+        line["short_prefill"] = [run_short_prefill(n, torch, A) for n in ("tiny", "tail128", "tail16")]
         if not args.no_fp8:
             fp8["short_prefill"] = [run_short_prefill(n, torch, A, kv_format="fp8")
-                                    for n in ("tail128", "tail16")]
+                                    for n in ("tiny", "tail128", "tail16")]
     if not args.no_short:
         line["repack"] = [run_repack_prefill(n, torch, A) for n in ("tail128", "tail16")]
     if not args.no_matrix:
