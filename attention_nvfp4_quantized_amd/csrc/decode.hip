@@ -201,8 +201,8 @@ __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int
 
 // Register sets of loads in rotation (kRing - 1 steps in flight while one is consumed) and
 // workgroups per CU for each cache format.  NVFP4: three sets at three workgroups, i.e. three
-// wavefronts per SIMD (158 registers).  FP8, whose sets are twice the size: five sets at two
-// workgroups (238 registers).  Measured against deeper rings and other occupancies, these were
+// wavefronts per SIMD (150 registers).  FP8, whose sets are twice the size: five sets at two
+// workgroups (236 registers).  Measured against deeper rings and other occupancies, these were
 // the fastest of the shapes that do not spill.
 template <int FMT>
 struct DecodeShape;

@@ -409,10 +409,10 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillParams& p, const P
 
 // ---- narrow kernel: NW wavefronts of 32 columns, two LDS buffers ---------------------------
 // Used for short query tiles, where the split-KV grid supplies the parallelism: NW = 4 (65..128
-// columns); up to 64 columns go to the key-split kernel below, more than 128 to the 8-wave kernel.  It asks for two workgroups per CU
-// (registers capped at 256: 232 for NVFP4, 246 for FP8, no spills; two tile buffers each fit the
-// LDS twice), which the host's split count assumes; the fp16 (repacked) form would spill there
-// and keeps one.
+// columns); up to 64 columns go to the key-split kernel below, more than 128 to the 8-wave
+// kernel.  It asks for two workgroups per CU (registers capped at 256: 232 for NVFP4, 246 for
+// FP8, no spills; two tile buffers each fit the LDS twice), which the host's split count
+// assumes; the fp16 (repacked) form would spill there and keeps one.
 template <int NW, int FMT>
 __global__ __launch_bounds__(64 * NW, FMT == kFmtF16 ? 1 : 2) void nvfp4_prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
