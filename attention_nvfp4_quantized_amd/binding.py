@@ -130,6 +130,22 @@ def _need(t, dtype, name):
 
 _IN_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 _OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 2}
+# attention outputs (prefill, decode): bf16 or float32 only
+_ATTN_OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+
+
+def _attn_out_code(dtype) -> int:
+    if dtype not in _ATTN_OUT_DTYPES:
+        raise TypeError(f"attention output must be bfloat16 or float32, got {dtype}")
+    return _ATTN_OUT_DTYPES[dtype]
+
+
+def _check_out(out, rows: int, hq: int, device):
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != device:
+        raise TypeError(f"out must be a CUDA tensor on {device}")
+    if tuple(out.shape) != (rows, hq, HEAD_DIM) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{rows}][{hq}][{HEAD_DIM}] tensor, "
+                         f"got {tuple(out.shape)}")
 
 
 def append(cache: NVFP4KVCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor):
@@ -197,15 +213,23 @@ def prefill(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
             sm_scale: float, causal: bool = True, out: torch.Tensor | None = None,
             out_dtype=torch.bfloat16, return_lse: bool = False, num_splits: int = 0,
             workspace: torch.Tensor | None = None):
-    """paged_prefill_nvfp4: q bf16 [total_q][Hq][128]; returns out (and lse if asked)."""
+    """paged_prefill_nvfp4: q bf16 [total_q][Hq][128]; returns out (and lse if asked).
+    out_dtype (or the dtype of a caller-supplied ``out``) must be bfloat16 or float32."""
+    odt = _attn_out_code(out_dtype if out is None else out.dtype)
     _need(q, torch.bfloat16, "q"); _need(cu_seqlens_q, torch.int32, "cu_seqlens_q")
     _need(kv_lens, torch.int32, "kv_lens"); _need(block_table, torch.int32, "block_table")
-    if not q.is_contiguous() or not block_table.is_contiguous():
-        raise ValueError("q and block_table must be contiguous")
+    if not q.is_contiguous() or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError("q and block_table must be contiguous (block_table [batch][stride])")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [total_q][Hq][{HEAD_DIM}], got {tuple(q.shape)}")
     total_q, hq = q.shape[0], q.shape[1]
     batch = kv_lens.numel()
+    if cu_seqlens_q.numel() != batch + 1 or block_table.shape[0] != batch:
+        raise ValueError(f"cu_seqlens_q must hold batch + 1 = {batch + 1} offsets and "
+                         f"block_table {batch} rows (one per kv_lens entry)")
     if out is None:
         out = torch.empty((total_q, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    _check_out(out, total_q, hq, q.device)
     lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if return_lse else None
     ws_bytes = prefill_workspace_size(batch, total_q, max_q_len, max_kv_len, hq, cache.num_kv_heads,
                                       num_splits)
@@ -215,7 +239,7 @@ def prefill(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     _check(load_library().paged_prefill_nvfp4(
         ctypes.byref(d), q.data_ptr(), cu_seqlens_q.data_ptr(), kv_lens.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], batch, total_q, max_q_len, max_kv_len, hq,
-        sm_scale, 1 if causal else 0, out.data_ptr(), 1 if out.dtype == torch.float32 else 0,
+        sm_scale, 1 if causal else 0, out.data_ptr(), odt,
         _ptr(lse), num_splits, _ptr(workspace) if ws_bytes else None, ws_bytes, _stream()))
     return (out, lse) if return_lse else out
 
@@ -229,14 +253,21 @@ def decode(cache: NVFP4KVCache, q: torch.Tensor, kv_lens: torch.Tensor, block_ta
            max_kv_len: int, sm_scale: float, out: torch.Tensor | None = None,
            out_dtype=torch.bfloat16, return_lse: bool = False, num_splits: int = 0,
            workspace: torch.Tensor | None = None):
-    """paged_decode_nvfp4: q bf16 [B][Hq][128]; returns out (and lse if asked)."""
+    """paged_decode_nvfp4: q bf16 [B][Hq][128]; returns out (and lse if asked).
+    out_dtype (or the dtype of a caller-supplied ``out``) must be bfloat16 or float32."""
+    odt = _attn_out_code(out_dtype if out is None else out.dtype)
     _need(q, torch.bfloat16, "q"); _need(kv_lens, torch.int32, "kv_lens")
     _need(block_table, torch.int32, "block_table")
-    if not q.is_contiguous() or not block_table.is_contiguous():
-        raise ValueError("q and block_table must be contiguous")
+    if not q.is_contiguous() or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError("q and block_table must be contiguous (block_table [batch][stride])")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [batch][Hq][{HEAD_DIM}], got {tuple(q.shape)}")
     batch, hq = q.shape[0], q.shape[1]
+    if kv_lens.numel() != batch or block_table.shape[0] != batch:
+        raise ValueError(f"kv_lens and block_table must have one entry / row per sequence ({batch})")
     if out is None:
         out = torch.empty((batch, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    _check_out(out, batch, hq, q.device)
     lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if return_lse else None
     ws_bytes = decode_workspace_size(batch, max_kv_len, hq, cache.num_kv_heads, num_splits)
     if workspace is None or workspace.numel() < ws_bytes:
@@ -245,6 +276,6 @@ def decode(cache: NVFP4KVCache, q: torch.Tensor, kv_lens: torch.Tensor, block_ta
     _check(load_library().paged_decode_nvfp4(
         ctypes.byref(d), q.data_ptr(), kv_lens.data_ptr(), block_table.data_ptr(),
         block_table.shape[1], batch, max_kv_len, hq, sm_scale, out.data_ptr(),
-        1 if out.dtype == torch.float32 else 0, _ptr(lse), num_splits, workspace.data_ptr(),
+        odt, _ptr(lse), num_splits, workspace.data_ptr(),
         workspace.numel(), _stream()))
     return (out, lse) if return_lse else out

@@ -11,14 +11,18 @@
 //
 // Exactness: the block scale is E4M3 round-to-nearest-even of the correctly rounded float32
 // quotient amax / 6 (saturating at 448), computed with integer operations on the float bits.
-// Element codes are E2M1 round-to-nearest-even (saturating at 6) of the exact quotient y / s.
-// The quotient of a bf16 value by an E4M3 scale either equals a rounding midpoint t * s
-// (t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}) exactly or differs from every midpoint by more
-// than 2^-9 relative: y has 8 significant bits and t * s at most 9, so a nonzero difference is
-// at least one unit of the coarser of the two.  The kernel forms q = y * fl32(1/s) (relative
-// error below 2^-22), corrects it once with the exact residual y - q s, which turns every exact
-// midpoint into exactly t, and rounds q to E2M1 with the hardware conversion (ties to even,
-// saturating).  Zeros keep their sign; a zero scale gives signed zeros.
+// Element codes are E2M1 round-to-nearest-even (saturating at 6) of the exact quotient y / s,
+// where y is a float32 value: x itself for bf16 (8 significant bits) or fp16 (11) input at g = 1,
+// fl32(x / g) (up to 24) otherwise.  The rounding midpoints t * s (t in {0.25, 0.75, 1.25, 1.75,
+// 2.5, 3.5, 5}, s with a 4-bit significand m_s in [1, 2)) are float32 numbers of at most 7
+// significant bits.  So either y = t * s exactly, or |y - t * s| >= ulp(y), which puts y / s
+// more than half a float32 ulp of t away from t (by the factor 2 / m_s > 1): at least 2^-24
+// relative.  The kernel forms q = y * fl32(1/s) (relative error below 2^-22), corrects it once
+// with the residual y - q s (exact: it has at most 6 significant bits), which leaves an error
+// below 2^-44 relative before the final float32 rounding.  A quotient off a midpoint therefore
+// rounds to a float32 value on the same side of t, and an exact midpoint comes out as exactly t;
+// the hardware conversion then rounds q to E2M1 (ties to even, saturating).  Zeros keep their
+// sign; a zero scale gives signed zeros.
 #include "device_common.hpp"
 #include "kernel_params.hpp"
 

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(DequantParams p) {
 // Dequantize-ahead repack ("NVFP4 KV cache A4Q prefill explained", section "Compare A4Q with
 // dequantize-ahead repacking": convert each NVFP4 tile once, before the attention kernel uses it
 // repeatedly): every page a sequence's keys occupy is converted to fp16 s * e2m1(code) (exact:
-// at most 5 significant bits, magnitude in [2^-10, 2688]) into a paged fp16 copy with the same
+// at most 6 significant bits, magnitude in [2^-10, 2688]) into a paged fp16 copy with the same
 // page ids.  The per-tensor scale g is not applied; the prefill over the copy applies it as it
 // does over the packed cache.  Grid: x = groups of 4 pages of a sequence, y = sequence,
 // z = KV head * 2 + (0 for K, 1 for V); a wavefront converts one page (lane l: quarter l%4 of

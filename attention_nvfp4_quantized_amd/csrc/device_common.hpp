@@ -95,8 +95,9 @@ __device__ __forceinline__ f32x2 pair32_values(float x) {
       : "+v"(a), "=&v"(b));
   return f32x2{a, b};
 }
-// fp16 read-side conversion.  Every NVFP4 value, E2M1 code times E4M3 scale, has at most 5
-// significant bits and a magnitude in [2^-10, 2688], so it is exact as a normal fp16 number.
+// fp16 read-side conversion.  Every NVFP4 value, E2M1 code times E4M3 scale, has at most 6
+// significant bits (2 from the code, 4 from the scale) and a magnitude in [2^-10, 2688], so it
+// is exact as a normal fp16 number (11 significant bits, normal from 2^-14).
 
 // Scale bytes 2*HI and 2*HI+1 of `word` -> fp16 pair (exact).
 template <bool HI>

@@ -378,6 +378,14 @@ def run_short_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
             "flop_per_call": flops, "bytes_per_call": int(nbytes)}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return None
+
+
 def run_cpu_baseline(pc, target_s=CPU_TARGET_S):
     """The oracle, untuned, on a bounded sample of the 16K prefill: all 32 heads of query rows
     spread evenly over the sequence (their visible keys included), after the oracle's append of
@@ -386,11 +394,7 @@ def run_cpu_baseline(pc, target_s=CPU_TARGET_S):
     about `target_s` seconds, so the sample is about that long on any host."""
     from oracle import attention as oattn
     from oracle import cache as ocache
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = None
+    blas_threads = _blas_threads()
     w = pc.w
     t0 = time.perf_counter()
     oc = ocache.PagedCache(pc.layout.num_pages, w.num_kv_heads)
@@ -421,6 +425,71 @@ def run_cpu_baseline(pc, target_s=CPU_TARGET_S):
                       "append of all 16,384 tokens (%.1f s, not in value)"
                       % (len(rows), flops, t_pre, t_append),
             "rows": int(len(rows)), "seconds": round(t_pre + t_append, 2)}
+
+
+def run_cpu_phases():
+    """The oracle, untuned and single-process as it stands, timed per phase beside the GPU legs:
+    the whole tiny and tail128 workloads (append of every token, then the prefill of every row),
+    one of the eight tail16 sequences (append of its 16,384 tokens, prefill of its 16 rows;
+    x 8 for the batch, labelled extrapolated), and one decode step of two sequences of the
+    decode workload (append of their step token, decode over 16K-32K keys; x 32 for the 64
+    sequences and x 64 for the loop, labelled extrapolated; the fill of their caches is set-up,
+    not timed)."""
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    out = {"blas_threads": _blas_threads(), "host_cores": len(os.sched_getaffinity(0))}
+    for name in ("tiny", "tail128"):
+        pc = prefill_case(name)
+        w = pc.w
+        t0 = time.perf_counter()
+        oc = ocache.PagedCache(pc.layout.num_pages, w.num_kv_heads)
+        oc.append(pc.k_bits, pc.v_bits, pc.slot_mapping)
+        t1 = time.perf_counter()
+        oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table, w.sm_scale)
+        t2 = time.perf_counter()
+        out[name] = {"append_s": round(t1 - t0, 3), "prefill_s": round(t2 - t1, 3),
+                     "total_s": round(t2 - t0, 3), "sample": "whole workload"}
+    pc = prefill_case("tail16")
+    w = pc.w
+    s0, s1 = int(pc.cu_seqlens_kv[0]), int(pc.cu_seqlens_kv[1])
+    t0 = time.perf_counter()
+    oc = ocache.PagedCache(pc.layout.num_pages, w.num_kv_heads)
+    oc.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1])
+    t1 = time.perf_counter()
+    oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table, w.sm_scale,
+                  rows=np.arange(int(pc.cu_seqlens_q[0]), int(pc.cu_seqlens_q[1])))
+    t2 = time.perf_counter()
+    out["tail16"] = {"append_s": round(t1 - t0, 3), "prefill_s": round(t2 - t1, 3),
+                     "total_s_extrapolated": round(8 * (t2 - t0), 3),
+                     "sample": "sequence 0 of 8 (16,384 tokens appended, 16 rows x 32 heads); "
+                               "total x 8, extrapolated"}
+    w = W.get("decode")
+    dc = W.decode_case(w)
+    lay = dc.layout
+    seqs = [int(np.argmin(w.kv_lens)), int(np.argmax(w.kv_lens))]
+    oc = ocache.PagedCache(lay.num_pages, w.num_kv_heads)
+    step_k = np.zeros((w.batch, w.num_kv_heads, 128), np.uint16)
+    step_v = np.zeros_like(step_k)
+    for b in seqs:
+        kb, vb = dc.seq_kv(b)
+        n = int(dc.init_lens[b]) - 1
+        oc.append(kb[:n], vb[:n], lay.slots(b, np.arange(n)), workers=min(16, out["host_cores"]))
+        step_k[b], step_v[b] = kb[n], vb[n]
+    slots = dc.step_slots(0)
+    t0 = time.perf_counter()
+    oc.append(step_k[seqs], step_v[seqs], slots[seqs])
+    t1 = time.perf_counter()
+    oattn.decode(oc, dc.step_q()[0], dc.step_kv_lens(0), lay.block_table, w.sm_scale, seqs=seqs)
+    t2 = time.perf_counter()
+    step = (t2 - t0) * w.batch / len(seqs)
+    out["decode"] = {"append_s": round(t1 - t0, 4), "decode_s": round(t2 - t1, 4),
+                     "kv_lens": [int(dc.step_kv_lens(0)[b]) for b in seqs],
+                     "step_s_extrapolated": round(step, 3),
+                     "loop_s_extrapolated": round(step * w.decode_steps, 2),
+                     "sample": "step 0 of sequences %s (shortest and longest); x %d for the 64 "
+                               "sequences and x 64 for the loop, extrapolated"
+                               % (seqs, w.batch // len(seqs))}
+    return out
 
 
 def fp8_summary(line, fp8):
@@ -484,7 +553,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "dtype_detail": "fp16 MFMA with fp32 accumulation (exact fp16 cache values; bf16 Q in, bf16 O out)",
         "data": "synthetic (seeded N(0,1) bf16, K outlier channels x8)",
         "config": {"workload": "full16k causal prefill + append", "batch": 1, "q_len": 16384,
                    "kv_len": 16384, "num_qo_heads": w.num_qo_heads,
@@ -520,6 +590,7 @@ def main():
         line["fp8_control"] = fp8_summary(line, fp8)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(pre["pc"])
+        line["cpu_baseline"]["phases"] = run_cpu_phases()
     print(json.dumps(line))
 
 

@@ -26,6 +26,9 @@ any result.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import contextlib
+
 import numpy as np
 
 from .cache import PagedCache
@@ -57,12 +60,30 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, last_visible: np.ndarray
     return o, lse
 
 
+def _run(tasks, workers: int):
+    """Run independent tasks (callables), in a thread pool when workers > 1 (each task then
+    uses one BLAS thread, so the pool does not oversubscribe the cores)."""
+    if workers <= 1:
+        for t in tasks:
+            t()
+        return
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas")
+    except ImportError:  # pragma: no cover
+        limit = contextlib.nullcontext()
+    with limit, cf.ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(t) for t in tasks]:
+            f.result()
+
+
 def prefill(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, block_table,
-            sm_scale: float, causal: bool = True, rows=None):
+            sm_scale: float, causal: bool = True, rows=None, heads=None, workers: int = 1):
     """Causal paged prefill.  q_bits: bf16 patterns [total_q][Hq][D].
 
-    ``rows`` (optional) lists the query-token indices to evaluate; the others
-    are left NaN.  Returns (o [total_q][Hq][D], lse [total_q][Hq]) in float64.
+    ``rows`` (optional) lists the query-token indices to evaluate, ``heads`` (optional) the
+    query heads; the others are left NaN.  ``workers`` > 1 evaluates (sequence, head) pairs in
+    that many threads.  Returns (o [total_q][Hq][D], lse [total_q][Hq]) in float64.
     """
     q = bf16_to_f32(q_bits).astype(np.float64)
     total_q, hq, d = q.shape
@@ -71,6 +92,7 @@ def prefill(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, block_
     lse = np.full((total_q, hq), np.nan)
     want = np.ones(total_q, bool) if rows is None else np.isin(np.arange(total_q), rows)
     cu = np.asarray(cu_seqlens_q)
+    tasks = []
     for b in range(len(kv_lens)):
         q0, q1, kvl = int(cu[b]), int(cu[b + 1]), int(kv_lens[b])
         idx = np.nonzero(want[q0:q1])[0]
@@ -79,29 +101,36 @@ def prefill(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, block_
         kh, vh = cache.gather(block_table[b], kvl)
         qlen = q1 - q0
         last = (kvl - qlen + idx) if causal else np.full(len(idx), kvl - 1)
-        for h in range(hq):
-            oh, lh = attend(q[q0 + idx, h], kh[:, h // group], vh[:, h // group], last, sm_scale)
-            o[q0 + idx, h] = oh
-            lse[q0 + idx, h] = lh
+        for h in (range(hq) if heads is None else heads):
+            def task(rows_=q0 + idx, h=h, kh=kh, vh=vh, last=last):
+                oh, lh = attend(q[rows_, h], kh[:, h // group], vh[:, h // group], last, sm_scale)
+                o[rows_, h] = oh
+                lse[rows_, h] = lh
+            tasks.append(task)
+    _run(tasks, workers)
     return o, lse
 
 
 def decode(cache: PagedCache, q_bits: np.ndarray, kv_lens, block_table, sm_scale: float,
-           seqs=None):
+           seqs=None, workers: int = 1):
     """Single-token decode: q_bits [B][Hq][D]; query b sees all kv_lens[b] keys.
 
-    ``seqs`` (optional) restricts the evaluation to those sequences.
+    ``seqs`` (optional) restricts the evaluation to those sequences; ``workers`` > 1 evaluates
+    the sequences in that many threads.
     """
     q = bf16_to_f32(q_bits).astype(np.float64)
     bsz, hq, d = q.shape
     group = hq // cache.num_kv_heads
     o = np.full((bsz, hq, d), np.nan)
     lse = np.full((bsz, hq), np.nan)
-    for b in (range(bsz) if seqs is None else seqs):
+
+    def one(b):
         kvl = int(kv_lens[b])
         kh, vh = cache.gather(block_table[b], kvl)
         for h in range(hq):
             oh, lh = attend(q[b, h][None, :], kh[:, h // group], vh[:, h // group],
                             np.array([kvl - 1]), sm_scale)
             o[b, h], lse[b, h] = oh[0], lh[0]
+
+    _run([lambda b=b: one(b) for b in (range(bsz) if seqs is None else seqs)], workers)
     return o, lse

@@ -18,9 +18,26 @@ one append call are assumed distinct.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+
 import numpy as np
 
 from . import codec
+
+_TOKENS_PER_TASK = 2048
+
+
+def map_tokens(fn, bits: np.ndarray, workers: int):
+    """fn over consecutive token chunks of ``bits`` (each token's result depends on that token
+    alone), in a thread pool when ``workers`` > 1; the chunk results joined in token order."""
+    if workers <= 1 or len(bits) <= _TOKENS_PER_TASK:
+        return fn(bits)
+    chunks = [bits[i:i + _TOKENS_PER_TASK] for i in range(0, len(bits), _TOKENS_PER_TASK)]
+    with cf.ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(fn, chunks))
+    if isinstance(parts[0], tuple):
+        return tuple(np.concatenate([p[i] for p in parts]) for i in range(len(parts[0])))
+    return np.concatenate(parts)
 
 
 class PagedCache:
@@ -40,18 +57,23 @@ class PagedCache:
         return sum(a.nbytes for a in (self.k_data, self.v_data, self.k_scale, self.v_scale))
 
     def append(self, k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray,
-               input_dtype: str = "bf16"):
+               input_dtype: str = "bf16", workers: int = 1):
         """Quantize bf16 or fp16 K/V ``[T][num_kv_heads][head_dim]`` (bit patterns) and write
         them to their slots ("NVFP4 KV cache A4Q prefill explained", section "Preserve the
-        capacity and decode case": the writer takes BF16 or FP16 input)."""
+        capacity and decode case": the writer takes BF16 or FP16 input).  ``workers`` > 1
+        quantizes chunks of tokens in that many threads (tokens are independent)."""
         slots = np.asarray(slot_mapping, dtype=np.int64)
         keep = slots >= 0
         page = slots[keep] // self.page_size
         off = slots[keep] % self.page_size
+
         for bits, data, scale, g in ((k_bits, self.k_data, self.k_scale, self.k_global),
                                      (v_bits, self.v_data, self.v_scale, self.v_global)):
-            codes, sc = codec.quantize(codec.input_to_f32(bits, input_dtype), g)
-            data[page, :, off, :] = codec.pack(codes)[keep]
+            def one(chunk, g=g):
+                codes, sc = codec.quantize(codec.input_to_f32(chunk, input_dtype), g)
+                return codec.pack(codes), sc
+            packed, sc = map_tokens(one, np.asarray(bits), workers)
+            data[page, :, off, :] = packed[keep]
             scale[page, :, off, :] = sc[keep]
 
     def token_rows(self, pages: np.ndarray, offsets: np.ndarray):

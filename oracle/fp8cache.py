@@ -15,6 +15,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import codec
+from .cache import map_tokens
 
 
 class Fp8PagedCache:
@@ -31,14 +32,16 @@ class Fp8PagedCache:
         return self.k_data.nbytes + self.v_data.nbytes
 
     def append(self, k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray,
-               input_dtype: str = "bf16"):
-        """Quantize bf16 or fp16 K/V ``[T][num_kv_heads][head_dim]`` and write their slots."""
+               input_dtype: str = "bf16", workers: int = 1):
+        """Quantize bf16 or fp16 K/V ``[T][num_kv_heads][head_dim]`` and write their slots
+        (``workers`` > 1: chunks of tokens in that many threads)."""
         slots = np.asarray(slot_mapping, dtype=np.int64)
         keep = slots >= 0
         page = slots[keep] // self.page_size
         off = slots[keep] % self.page_size
         for bits, data, g in ((k_bits, self.k_data, self.k_global), (v_bits, self.v_data, self.v_global)):
-            codes = codec.quantize_fp8(codec.input_to_f32(bits, input_dtype), g)
+            codes = map_tokens(lambda c, g=g: codec.quantize_fp8(codec.input_to_f32(c, input_dtype), g),
+                               np.asarray(bits), workers)
             data[page, :, off, :] = codes[keep]
 
     def dequant_slots(self, slot_mapping: np.ndarray, out_dtype: str = "bf16"):

@@ -3,6 +3,8 @@ and build the matching oracle cache.  Inputs come only from ``workload``; expect
 from ``oracle``."""
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 import sys
 
 import numpy as np
@@ -15,15 +17,21 @@ from oracle import cache as ocache
 from oracle import fp8cache as ofp8
 
 DEV = "cuda"
+# host threads for the oracle's token and (sequence, head) maps
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 # Output tolerance on attention (float32 output): the bar the path is held to.
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 # log-sum-exp: the kernels sum the rounded softmax weights (the same weights the PV product
-# uses: fp16 rounded toward zero, relative error below 2^-10); each is within a relative 2^-9 of
-# its float value, so the sum is too and its log is within 2^-9 absolute.  Plus float32
-# rounding of the rest.
-LSE_ATOL = 2.0 ** -9 + 5e-4
+# uses: fp16 rounded toward zero).  A weight in fp16's normal range (>= 2^-14) loses less than
+# 2^-10 of itself; the largest weight of a row is >= 1, so the row sum S is >= 1 and the sum of
+# the rounded weights lies within a relative 2^-10 of S, its log within 2^-10 (natural log;
+# -ln(1 - 2^-10) < 2^-10 + 2^-20).  Weights below 2^-14 (fp16 subnormal) lose less than 2^-24
+# each, absolute, a relative 2^-24 of S per key: at most 1/8 of 2^-10 even if every key of a
+# 2,048-key row were that small (a score 14 below the row maximum in base 2), and the rows tested
+# here have a few.  Plus float32 rounding of the scores, the maximum and the log: 5e-4.
+LSE_ATOL = 2.0 ** -10 + 5e-4
 
 
 def say(*a):
@@ -78,7 +86,7 @@ def oracle_cache(pc: W.PrefillCase, seqs=None, k_global=1.0, v_global=1.0, kv_fo
     seqs = range(pc.w.batch) if seqs is None else seqs
     for b in seqs:
         s0, s1 = pc.cu_seqlens_kv[b], pc.cu_seqlens_kv[b + 1]
-        c.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1])
+        c.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1], workers=WORKERS)
     return c
 
 
@@ -137,55 +145,110 @@ def assert_attention_close_bf16(gpu: np.ndarray, ref: np.ndarray, what: str, max
 
 def oracle_prefill(pc: W.PrefillCase, oc: ocache.PagedCache, rows=None, causal=True):
     return oattn.prefill(oc, pc.q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
-                         pc.w.sm_scale, causal=causal, rows=rows)
+                         pc.w.sm_scale, causal=causal, rows=rows, workers=WORKERS)
 
 
 def rows_of(pc: W.PrefillCase, seqs) -> np.ndarray:
     return np.concatenate([np.arange(pc.cu_seqlens_q[b], pc.cu_seqlens_q[b + 1]) for b in seqs])
 
 
+def spread_sequences(lens, n: int) -> list:
+    """n sequence indices spread over the range of lengths (sorted-length quantiles)."""
+    order = np.argsort(np.asarray(lens), kind="stable")
+    return sorted({int(order[i]) for i in np.linspace(0, len(order) - 1, n).round().astype(int)})
+
+
 class DecodeRun:
-    """The decode workload at full size: 64 sequences, 64 steps of (append 64 tokens, decode).
+    """The decode workload at full size and in the launch configuration the benchmark times:
+    64 sequences, each with its seeded K/V, 64 steps of (append one token per sequence, decode
+    with bf16 output).  At the checked steps the decode is also run with float32 output.  Keeps
+    the step tokens of every sequence and the whole K/V of ``oracle_seqs``; after the loop,
+    ``step_rows`` holds the cache rows of every step-appended slot and ``seq_pages`` the cache
+    pages of the oracle sequences, read back from the device."""
 
-    Sampled sequences carry their seeded K/V; the others keep zero K/V, which changes none of
-    the sampled outputs (sequences are independent) and none of the launch shapes."""
-
-    def __init__(self, sampled, check_steps, kv_format="nvfp4"):
+    def __init__(self, oracle_seqs, check_steps, kv_format="nvfp4"):
         self.w = W.get("decode")
         self.dc = W.decode_case(self.w)
         self.kv_format = kv_format
+        self.oracle_seqs = list(oracle_seqs)
         lay, w = self.dc.layout, self.w
+        steps = w.decode_steps
         self.cache = A.NVFP4KVCache(lay.num_pages, w.num_kv_heads, kv_format=kv_format)
-        self.kv_bits = {b: self.dc.seq_kv(b) for b in sampled}
-        for b, (k, v) in self.kv_bits.items():
-            n = int(self.dc.init_lens[b]) - 1
-            A.append(self.cache, dev_bf16(k[:n]), dev_bf16(v[:n]), dev(lay.slots(b, np.arange(n))))
+        self.kv_bits = {}
+        self.step_k = np.zeros((steps, w.batch, w.num_kv_heads, w.head_dim), np.uint16)
+        self.step_v = np.zeros_like(self.step_k)
+
+        def draw(b):
+            return b, self.dc.seq_kv(b)
+
+        with cf.ThreadPoolExecutor(WORKERS) as ex:
+            for b0 in range(0, w.batch, WORKERS):  # a pool's worth at a time bounds host memory
+                for b, (k, v) in ex.map(draw, range(b0, min(w.batch, b0 + WORKERS))):
+                    n = int(self.dc.init_lens[b]) - 1
+                    A.append(self.cache, dev_bf16(k[:n]), dev_bf16(v[:n]), dev(lay.slots(b, np.arange(n))))
+                    self.step_k[:, b], self.step_v[:, b] = k[n:n + steps], v[n:n + steps]
+                    if b in self.oracle_seqs:
+                        self.kv_bits[b] = (k, v)
+                torch.cuda.synchronize()
         q_all = self.dc.step_q()
         bt = dev(lay.block_table)
-        self.out = {}
-        max_kv = int(self.dc.init_lens.max()) + w.decode_steps - 1
-        zeros = np.zeros((w.batch, w.num_kv_heads, w.head_dim), np.uint16)
-        for t in range(w.decode_steps):
-            kb, vb = zeros.copy(), zeros.copy()
-            for b, (k, v) in self.kv_bits.items():
-                kb[b], vb[b] = k[int(self.dc.init_lens[b]) - 1 + t], v[int(self.dc.init_lens[b]) - 1 + t]
-            A.append(self.cache, dev_bf16(kb), dev_bf16(vb), dev(self.dc.step_slots(t)))
-            o = A.decode(self.cache, dev_bf16(q_all[t]), dev(self.dc.step_kv_lens(t)), bt, max_kv,
-                         w.sm_scale, out_dtype=torch.float32)
+        self.out, self.out_bf16 = {}, {}
+        max_kv = int(self.dc.init_lens.max()) + steps - 1
+        self.step_slots = np.stack([self.dc.step_slots(t) for t in range(steps)])
+        for t in range(steps):
+            A.append(self.cache, dev_bf16(self.step_k[t]), dev_bf16(self.step_v[t]),
+                     dev(self.step_slots[t]))
+            q, lens = dev_bf16(q_all[t]), dev(self.dc.step_kv_lens(t))
+            o16 = A.decode(self.cache, q, lens, bt, max_kv, w.sm_scale, out_dtype=torch.bfloat16)
             if t in check_steps:
-                self.out[t] = o.cpu().numpy()
+                self.out_bf16[t] = o16.float().cpu().numpy()
+                self.out[t] = A.decode(self.cache, q, lens, bt, max_kv, w.sm_scale,
+                                       out_dtype=torch.float32).cpu().numpy()
         torch.cuda.synchronize()
         self.q_all = q_all
+        flat = torch.from_numpy(self.step_slots.reshape(-1)).to(DEV)
+        pg, off = flat // 16, flat % 16
+        self.step_rows = [t[pg, :, off, :].cpu().numpy() for t in self._planes()]
+        pages = np.concatenate([seq_pages_of(lay, b, int(self.dc.init_lens[b]) + steps - 1)
+                                for b in self.oracle_seqs])
+        self.oracle_pages = pages
+        idx = torch.from_numpy(pages.astype(np.int64)).to(DEV)
+        self.seq_pages = [t[idx].cpu().numpy() for t in self._planes()]
 
-    def oracle(self, steps, sampled):
-        """Oracle outputs at the given steps; its cache holds every token up to the last step
-        (a decode at step t reads only the first L_b + t of them)."""
+    def _planes(self):
+        c = self.cache
+        return [t for t in (c.k_data, c.k_scale, c.v_data, c.v_scale) if t is not None]
+
+    def oracle_cache(self):
+        """Oracle cache holding the whole K/V of the oracle sequences (every position up to the
+        last step) and the step tokens of every sequence."""
         lay = self.dc.layout
         make = ofp8.Fp8PagedCache if self.kv_format == "fp8" else ocache.PagedCache
         oc = make(lay.num_pages, self.w.num_kv_heads)
-        for b in sampled:
+        for b in self.oracle_seqs:
             k, v = self.kv_bits[b]
-            n = int(self.dc.init_lens[b]) + max(steps)
-            oc.append(k[:n], v[:n], lay.slots(b, np.arange(n)))
-        return {t: oattn.decode(oc, self.q_all[t], self.dc.step_kv_lens(t), lay.block_table,
-                                self.w.sm_scale, seqs=sampled)[0] for t in steps}
+            n = int(self.dc.init_lens[b]) + self.w.decode_steps - 1
+            oc.append(k[:n], v[:n], lay.slots(b, np.arange(n)), workers=WORKERS)
+        oc.append(self.step_k.reshape(-1, *self.step_k.shape[2:]),
+                  self.step_v.reshape(-1, *self.step_v.shape[2:]), self.step_slots.reshape(-1),
+                  workers=WORKERS)
+        return oc
+
+    def oracle(self, oc, steps):
+        """Oracle outputs of the oracle sequences at the given steps (a decode at step t reads
+        the first L_b + t tokens of the cache)."""
+        return {t: oattn.decode(oc, self.q_all[t], self.dc.step_kv_lens(t), self.dc.layout.block_table,
+                                self.w.sm_scale, seqs=self.oracle_seqs, workers=WORKERS)[0]
+                for t in steps}
+
+
+def seq_pages_of(layout: W.PageLayout, b: int, n_tokens: int) -> np.ndarray:
+    return layout.block_table[b][: (n_tokens + 15) // 16]
+
+
+def oracle_rows(oc, slots: np.ndarray):
+    """The oracle cache's rows of the given slots, in the order of ``DecodeRun.step_rows``."""
+    pg, off = slots // 16, slots % 16
+    names = ("k_data", "v_data") if isinstance(oc, ofp8.Fp8PagedCache) else (
+        "k_data", "k_scale", "v_data", "v_scale")
+    return [getattr(oc, n)[pg, :, off, :] for n in names]

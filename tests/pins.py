@@ -407,3 +407,183 @@ def check_attention_bruteforce(codec, cache_mod, attention, seed=7, head_dim=32,
                 ref_o, ref_l = brute_force_attention(qv, kd, vd, [kl - ql + i for i in range(ql)], sm)
                 np.testing.assert_allclose(o[cu[b]:cu[b + 1], h], ref_o, rtol=0, atol=1e-12)
                 np.testing.assert_allclose(lse[cu[b]:cu[b + 1], h], ref_l, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# Per-tensor scale g != 1 ("NVFP4 KV cache vs NVFP4 weights": a second, per-tensor scale maps
+# the tensor into the range the block format covers; the writer divides by it, the reader
+# multiplies by it)
+# ---------------------------------------------------------------------------------------
+
+def rne32(x: Fraction) -> Fraction:
+    """x rounded to the nearest float32 (ties to even), normal and subnormal range."""
+    return nearest_even_fraction(x, -126, 23)
+
+
+_E2M1_MIDPOINTS = [Fraction(1, 4), Fraction(3, 4), Fraction(5, 4), Fraction(7, 4), Fraction(5, 2),
+                   Fraction(7, 2), Fraction(5)]
+
+
+def expected_block(xs, g: Fraction, table=None):
+    """Scale code and element codes of one 16-value block of float32 inputs under per-tensor
+    scale g, by exact rationals: y = RNE32(x / g); s = E4M3(RNE32(amax_y / 6)); magnitude code =
+    number of midpoints below |y| / s (a midpoint itself counts when the lower grid code is odd,
+    which sends ties to the even code); sign bit copied from y (from x, as g > 0)."""
+    table = table or _fraction_e4m3_table()
+    ys = [rne32(Fraction(float(x)) / g) for x in xs]
+    amax = max(abs(y) for y in ys)
+    sc = expected_e4m3_code(rne32(amax / 6), table)
+    s = table[sc]
+    codes = []
+    for x, y in zip(xs, ys):
+        mag = 0
+        if s > 0:
+            r = abs(y) / s
+            for i, t in enumerate(_E2M1_MIDPOINTS):
+                if r > t or (r == t and i % 2 == 1):
+                    mag += 1
+        codes.append((8 if math.copysign(1.0, float(x)) < 0 else 0) | mag)
+    return sc, codes
+
+
+def near_threshold_inputs(g: float, seed=31, n=192) -> np.ndarray:
+    """Float32 blocks whose quotients x / g sit within a few float32 ulps of an E2M1 rounding
+    midpoint t * s (x = fl32(t s g) and its float32 neighbours), each block holding 6 s g so that
+    its scale is s (or one code away): inputs on which y = fl32(x / g) and the exact x / g round
+    differently."""
+    rng = np.random.default_rng(seed)
+    out = np.zeros((n, 16), np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for i in range(n):
+        s = float(2.0 ** rng.integers(-8, 6) * (1 + rng.integers(0, 8) / 8))
+        out[i, 0] = np.float32(6 * s * g)
+        t = mids[rng.integers(0, 7, 15)]
+        base = (t * s * g).astype(np.float32)
+        step = rng.integers(-3, 4, 15)
+        vals = np.array([np.nextafter(b, np.float32(np.inf) if k > 0 else np.float32(-np.inf))
+                         if k else b for b, k in zip(base, step)], np.float32)
+        for j, k in enumerate(step):  # |k| float32 steps
+            for _ in range(abs(int(k)) - 1):
+                vals[j] = np.nextafter(vals[j], np.float32(np.inf) if k > 0 else np.float32(-np.inf))
+        out[i, 1:] = vals * np.where(rng.random(15) < 0.5, -1, 1).astype(np.float32)
+    return out
+
+
+def check_quantize_general_g(codec, gs=(float(np.float32(1 / 3)), 1.5, 0.75), seed=32):
+    """codec.quantize at non-power-of-two g against exact rationals (y = RNE32(x / g), then the
+    block rule), on random blocks over a wide range and on blocks built next to rounding
+    midpoints."""
+    rng = np.random.default_rng(seed)
+    table = _fraction_e4m3_table()
+    for g in gs:
+        gf = Fraction(g)
+        rand = (rng.standard_normal((160, 16)) * np.exp(rng.uniform(-12, 9, (160, 1)))).astype(np.float32)
+        rand[0] = 0.0
+        rand[1, ::2] = -0.0
+        x = np.concatenate([rand, near_threshold_inputs(g, seed=seed + int(g * 1000))])
+        codes, sc = codec.quantize(x, g)
+        for i in range(x.shape[0]):
+            esc, ecodes = expected_block(x[i], gf, table)
+            assert int(sc[i, 0]) == esc, (g, i, int(sc[i, 0]), esc)
+            assert [int(c) for c in codes[i]] == ecodes, (g, i, list(codes[i]), ecodes)
+
+
+# g pairs (K, V) for the NVFP4 dequantization pin: fl32(1/3) and 1.5 are plain non-powers of two;
+# 2.8187499 (bf16 output) and 1.1714844 (fp16 output) are float32 values for which a product
+# s * e2m1 * g rounded first to float32 and then to the output type differs from rounding the
+# exact product once (19 of the 127 x 7 magnitudes each), so the pin sees the float32 step.
+DEQUANT_G_PAIRS = ((float(np.float32(1 / 3)), 1.5), (2.8187499046325684, 1.171484351158142))
+
+
+def check_nvfp4_dequant_general_g(codec, cache_mod, g_pairs=DEQUANT_G_PAIRS):
+    """NVFP4 standalone dequantization at g != 1 of every element code under every scale code,
+    against exact rationals: RNE32(s * e2m1(code) * g) (s * e2m1 is exact), then nearest-even to
+    the output type; slot < 0 gives zero rows."""
+    table = _fraction_e4m3_table()
+    grid = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+            Fraction(4), Fraction(6)]
+    fmts = {"bf16": (-126, 7, bf16_value), "fp16": (-14, 10, fp16_value_by_fields),
+            "f32": (-126, 23, None)}
+    memo = {}
+
+    def expected(sc, e, g, out):
+        key = (sc, e, g, out)
+        if key not in memo:
+            exact = (-1 if e & 8 else 1) * table[sc] * grid[e & 7] * Fraction(g)
+            memo[key] = nearest_even_fraction(rne32(exact), fmts[out][0], fmts[out][1])
+        return memo[key]
+
+    for gk, gv in g_pairs:
+        c = cache_mod.PagedCache(8, 2, k_global=gk, v_global=gv)
+        # 127 scale codes x 16 element codes: token t of page p, head h holds scale code
+        # (8 (16 p + t) + 4 h + block) % 127 in block `block`, and every block holds all 16
+        # element codes (a rotated 0..15 ramp)
+        nslots = 8 * 16
+        codes = np.tile(np.arange(16, dtype=np.uint8), 8)
+        packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+        for slot in range(nslots):
+            p, t = divmod(slot, 16)
+            for h in range(2):
+                for plane_d, plane_s in ((c.k_data, c.k_scale), (c.v_data, c.v_scale)):
+                    plane_d[p, h, t] = np.roll(packed, slot % 7)
+                    plane_s[p, h, t] = [(8 * slot + 4 * h + bb) % 127 for bb in range(8)]
+        slots = np.concatenate([np.arange(nslots), [-1]]).astype(np.int64)
+        for out, (_, _, decode) in fmts.items():
+            k, v = c.dequant_slots(slots, out)
+            for got, data, scale, g in ((k, c.k_data, c.k_scale, gk), (v, c.v_data, c.v_scale, gv)):
+                vals = np.asarray(got if decode is None else decode(got), np.float64)
+                for slot in range(nslots):
+                    p, t = divmod(slot, 16)
+                    for h in range(2):
+                        row = data[p, h, t]
+                        el = np.empty(128, np.int64)
+                        el[0::2], el[1::2] = row & 0xF, row >> 4
+                        for j in range(128):
+                            exp = expected(int(scale[p, h, t, j // 16]), int(el[j]), g, out)
+                            assert Fraction(float(vals[slot, h, j])) == exp, (out, g, slot, h, j)
+                assert not np.any(vals[-1]), out
+
+
+def expected_nvfp4_dual_row(q_row):
+    """Two-level NVFP4 quantization of one float32 query row by exact rationals: g =
+    RNE32(amax / RNE32(6 * 448)) (1 for a zero row); y = RNE32(q / g); each 16-block of y gets
+    s = E4M3(RNE32(amax_b / 6)) and E2M1 nearest-even codes; value g * s * e2m1 (no further
+    rounding)."""
+    table = _fraction_e4m3_table()
+    fr = [Fraction(float(x)) for x in q_row]
+    amax = max(abs(x) for x in fr)
+    g = rne32(amax / rne32(Fraction(6 * 448))) if amax > 0 else Fraction(1)
+    out = []
+    grid = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+            Fraction(4), Fraction(6)]
+    for b0 in range(0, len(fr), 16):
+        ys = [rne32(x / g) for x in fr[b0:b0 + 16]]
+        s = table[expected_e4m3_code(rne32(max(abs(y) for y in ys) / 6), table)]
+        for y in ys:
+            mag = 0
+            if s > 0:
+                r = abs(y) / s
+                for i, t in enumerate(_E2M1_MIDPOINTS):
+                    if r > t or (r == t and i % 2 == 1):
+                        mag += 1
+            out.append(float((-1 if y < 0 else 1) * grid[mag] * s * g))
+    return out
+
+
+def dual_level_rows(seed=33) -> np.ndarray:
+    """Query rows for the two-level pin: N(0,1) rows over a wide range of magnitudes, zero rows,
+    and rows whose blocks span many binades (some blocks 2^-10 .. 2^-20 of the row maximum, where
+    the level-one scale decides whether their block scales are normal or subnormal)."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((40, 128)) * np.exp(rng.uniform(-30, 30, (40, 1)))).astype(np.float32)
+    x[0] = 0.0
+    for i in range(1, 12):
+        x[i] *= np.repeat(np.float32(2.0) ** -rng.integers(0, 21, 8), 16).astype(np.float32)
+    return x
+
+
+def check_nvfp4_dual(a4q_mod):
+    x = dual_level_rows()
+    got = a4q_mod.quantize_q(x, "nvfp4_dual")
+    for i in range(x.shape[0]):
+        assert list(got[i]) == expected_nvfp4_dual_row(x[i]), i

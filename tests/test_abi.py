@@ -216,3 +216,18 @@ def test_f16_format_is_prefill_only():
     assert lib.paged_decode_nvfp4(ctypes.byref(d), 16, 16, 16, 2048, 64, 32768, 32, 0.088, 16, 0,
                                   None, 0, 16, 1 << 40, None) == -2
     assert _prefill(lib, d, total_q=0) == 0
+
+
+def test_binding_rejects_fp16_attention_output():
+    """Attention outputs are bf16 or float32: an fp16 out_dtype, or a caller's fp16 `out`, is
+    refused before any device call (the C ABI would otherwise be told bf16 and write bf16 bit
+    patterns into a float16 tensor)."""
+    import torch
+    for fn, args in ((A.prefill, (None, None, None, None, None, 16, 16, 0.088)),
+                     (A.decode, (None, None, None, None, 16, 0.088))):
+        with pytest.raises(TypeError, match="bfloat16 or float32"):
+            fn(*args, out_dtype=torch.float16)
+        with pytest.raises(TypeError, match="bfloat16 or float32"):
+            fn(*args, out=torch.empty((1, 1, 128), dtype=torch.float16))
+        with pytest.raises(TypeError, match="bfloat16 or float32"):
+            fn(*args, out_dtype=torch.int32)

@@ -12,7 +12,7 @@ import workload as W
 from oracle import fp8cache as ofp8
 from gpu_cases import (DEV, LSE_ATOL, DecodeRun, GpuPrefillCase, assert_attention_close,
                        assert_attention_close_bf16, assert_cache_equal, cache_planes, dev,
-                       dev_bf16, oracle_cache, oracle_prefill, say)
+                       dev_bf16, oracle_cache, oracle_prefill, oracle_rows, say, spread_sequences)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,15 +120,21 @@ def test_fp8_prefill_full16k_sampled_rows():
     assert_attention_close(o32, ref, "fp8 full16k fp32")
 
 
-def test_fp8_decode_parity_full_size_sampled_sequences():
+def test_fp8_decode_parity_full_size():
+    """The decode workload over the FP8 cache: all 64 sequences with their seeded K/V; the bytes
+    of every step-appended slot, and both output types of four sequences spread over the length
+    range at the first and last step."""
     w = W.get("decode")
-    lens = np.asarray(w.kv_lens)
-    sampled = [int(lens.argmin()), int(lens.argmax())]
-    say(f"[fp8 decode] 64 steps, sampled sequences {sampled}")
-    run = DecodeRun(sampled, check_steps=(0, 63), kv_format="fp8")
-    refs = run.oracle((0, 63), sampled)
+    seqs = spread_sequences(w.kv_lens, 4)
+    say(f"[fp8 decode] 64 sequences x 64 steps, oracle sequences {seqs}")
+    run = DecodeRun(seqs, check_steps=(0, 63), kv_format="fp8")
+    oc = run.oracle_cache()
+    for name, got, e in zip(("k_data", "v_data"), run.step_rows, oracle_rows(oc, run.step_slots.reshape(-1))):
+        assert np.array_equal(got, e), name
+    refs = run.oracle(oc, (0, 63))
     for t in (0, 63):
-        assert_attention_close(run.out[t], refs[t], f"fp8 decode step {t}")
+        assert_attention_close(run.out[t], refs[t], f"fp8 decode step {t} fp32")
+        assert_attention_close_bf16(run.out_bf16[t], refs[t], f"fp8 decode step {t} bf16")
 
 
 def test_fp8_append_skipped_slots_and_global_scales():

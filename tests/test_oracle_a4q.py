@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import a4q, cache, codec
+import pins
 
 GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
         Fraction(4), Fraction(6)]
@@ -139,3 +140,101 @@ def test_pins_catch_mx_scale_one_exponent_high():
     with pytest.raises(AssertionError):
         for i in range(4):
             assert list(bad(x[i])) == _mx_block_brute(x[i])
+
+
+def _nvfp4_row_brute(row):
+    """One-level NVFP4 value of a float32 row by exact rationals (the block rule at g = 1)."""
+    out = []
+    table = pins._fraction_e4m3_table()
+    for b0 in range(0, len(row), 16):
+        sc, codes = pins.expected_block(row[b0:b0 + 16], Fraction(1), table)
+        for c in codes:
+            out.append(float((-1 if c & 8 else 1) * GRID[c & 7] * table[sc]))
+    return out
+
+
+def _quantize_brute(row, scheme):
+    if scheme == "mxfp4":
+        return [v for j in range(0, len(row), 32) for v in _mx_block_brute(row[j:j + 32])]
+    if scheme == "nvfp4":
+        return _nvfp4_row_brute(row)
+    return pins.expected_nvfp4_dual_row(row)
+
+
+def check_prefill_a4q_paged(prefill_a4q, scheme, seed=26):
+    """prefill_a4q on a paged, ragged, GQA (2 query heads per KV head), causal batch against
+    Python loops: each query row quantized by the exhaustive / exact-rational quantizers above, K
+    and V dequantized independently of the page table, scores and weights as Python floats,
+    weights rounded to bf16 for the PV sum and the normaliser from the unrounded weights."""
+    rng = np.random.default_rng(seed)
+    d, hq, hkv, ps = 64, 4, 2, 16
+    q_lens, kv_lens = [2, 5, 1], [3, 21, 17]
+    pages = [(n + ps - 1) // ps for n in kv_lens]
+    perm = rng.permutation(sum(pages) + 3)
+    bt = np.zeros((3, max(pages)), np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[off:off + n]; off += n
+    oc = cache.PagedCache(sum(pages) + 3, hkv, head_dim=d, page_size=ps)
+    sm = 1 / math.sqrt(d)
+    kd, vd, qs = [], [], []
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        k = (rng.standard_normal((kl, hkv, d)) * 2).astype(np.float32)
+        v = rng.standard_normal((kl, hkv, d)).astype(np.float32)
+        kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+        vb = (v.view(np.uint32) >> 16).astype(np.uint16)
+        pos = np.arange(kl)
+        oc.append(kb, vb, bt[b][pos // ps].astype(np.int64) * ps + pos % ps)
+        rt = lambda bits: np.array([_nvfp4_row_brute(pins.bf16_value(r)) for r in bits.reshape(-1, d)]).reshape(kl, hkv, d)  # noqa: E731
+        kd.append(rt(kb)); vd.append(rt(vb))
+        qs.append((rng.standard_normal((ql, hq, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    qb = np.concatenate(qs)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    got = prefill_a4q(oc, qb, cu, kv_lens, bt, sm, scheme)
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        for h in range(hq):
+            kvh = h // (hq // hkv)
+            for i in range(ql):
+                qv = _quantize_brute(pins.bf16_value(qs[b][i, h]), scheme)
+                last = kl - ql + i
+                z = [sm * math.fsum(qv[t] * kd[b][j, kvh, t] for t in range(d)) for j in range(last + 1)]
+                zm = max(z)
+                p = [math.exp(x - zm) for x in z]
+                den = math.fsum(p)
+                for t in range(d):
+                    ref = math.fsum(_bf16(p[j]) * vd[b][j, kvh, t] for j in range(len(p))) / den
+                    assert abs(got[cu[b] + i, h, t] - ref) < 1e-12, (scheme, b, h, i, t)
+
+
+@pytest.mark.parametrize("scheme", a4q.SCHEMES)
+def test_prefill_a4q_paged_ragged_vs_brute_force(scheme):
+    check_prefill_a4q_paged(a4q.prefill_a4q, scheme)
+
+
+def test_nvfp4_dual_vs_exact_rationals():
+    pins.check_nvfp4_dual(a4q)
+
+
+def test_pins_catch_prefill_a4q_top_left_mask():
+    def top_left(oc, qb, cu, kv_lens, bt, sm, scheme):  # rows see keys 0..i (top-left alignment)
+        o = np.full((int(cu[-1]), 4, 64), np.nan)
+        for b in range(len(kv_lens)):
+            q0, q1 = int(cu[b]), int(cu[b + 1])
+            sub = a4q.prefill_a4q(oc, qb[q0:q1], np.array([0, q1 - q0], np.int32), [q1 - q0],
+                                  bt[b:b + 1], sm, scheme)
+            o[q0:q1] = sub
+        return o
+    with pytest.raises(AssertionError):
+        check_prefill_a4q_paged(top_left, "mxfp4")
+
+
+def test_pins_catch_dual_level_without_the_448():
+    def bad(q, scheme):
+        q32 = np.asarray(q, np.float32)
+        amax = np.abs(q32).max(axis=-1, keepdims=True)
+        g = (amax / np.float32(6.0)).astype(np.float32)
+        g = np.where(g > 0, g, np.float32(1.0)).astype(np.float32)
+        return a4q._nvfp4_values((q32 / g).astype(np.float32)) * g.astype(np.float64)
+    import types
+    with pytest.raises(AssertionError):
+        pins.check_nvfp4_dual(types.SimpleNamespace(quantize_q=bad))

@@ -215,3 +215,44 @@ def test_pins_catch_repack_applying_the_global_scale():
     import types
     with pytest.raises(AssertionError):
         pins.check_repack(codec, types.SimpleNamespace(PagedCache=C))
+
+
+def test_quantize_at_non_power_of_two_g_vs_exact_rationals():
+    pins.check_quantize_general_g(codec)
+
+
+def test_nvfp4_dequant_at_g_not_one_vs_exact_rationals():
+    pins.check_nvfp4_dequant_general_g(codec, cache)
+
+
+def test_pins_catch_quantize_without_float32_quotient():
+    def q64(x, g=1.0):  # y = x / g kept in float64: no float32 rounding of the quotient
+        y = np.asarray(x, np.float32).astype(np.float64) / g
+        yb = y.reshape(*y.shape[:-1], y.shape[-1] // 16, 16)
+        sc = codec.e4m3_encode(np.abs(yb).max(axis=-1) / 6.0)
+        return codec.e2m1_encode(y, np.repeat(codec.e4m3_value(sc), 16, axis=-1)), sc
+    with pytest.raises(AssertionError):
+        pins.check_quantize_general_g(_Mutant(quantize=q64))
+
+
+def test_pins_catch_dequant_without_float32_product():
+    class C(cache.PagedCache):
+        def dequant_slots(self, slot_mapping, out_dtype="bf16"):
+            k, v = super().dequant_slots(slot_mapping, "f32")
+            out = []
+            for x, data, scale, g in ((k, self.k_data, self.k_scale, self.k_global),
+                                      (v, self.v_data, self.v_scale, self.v_global)):
+                slots = np.asarray(slot_mapping, np.int64)
+                keep = slots >= 0
+                pg, off = np.where(keep, slots // 16, 0), np.where(keep, slots % 16, 0)
+                s = np.repeat(codec.e4m3_value(scale[pg, :, off, :]), 16, axis=-1)
+                ex = np.where(keep[:, None, None], s * codec.e2m1_value(codec.unpack(data[pg, :, off, :])) * g, 0)
+                if out_dtype == "bf16":  # exact product rounded once, straight to bf16
+                    m, e = np.frexp(ex)
+                    out.append(codec.round_to_dtype(np.ldexp(np.round(np.ldexp(m, 8)), e - 8).astype(np.float32), "bf16"))
+                else:
+                    out.append(codec.round_to_dtype(ex.astype(np.float32), out_dtype))
+            return out[0], out[1]
+    import types
+    with pytest.raises(AssertionError):
+        pins.check_nvfp4_dequant_general_g(codec, types.SimpleNamespace(PagedCache=C))
