@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_decode_nvfp4_workspace_size.restype = SZ
     lib.paged_decode_nvfp4.argtypes = [C, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P]
     lib.paged_decode_nvfp4.restype = ctypes.c_int
+    lib.paged_decode_nvfp4_noalloc.argtypes = [C, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P]
+    lib.paged_decode_nvfp4_noalloc.restype = ctypes.c_int
     lib.nvfp4kv_last_error.argtypes = []
     lib.nvfp4kv_last_error.restype = ctypes.c_char_p
     lib.nvfp4kv_version.argtypes = []
@@ -278,4 +280,36 @@ def decode(cache: NVFP4KVCache, q: torch.Tensor, kv_lens: torch.Tensor, block_ta
         block_table.shape[1], batch, max_kv_len, hq, sm_scale, out.data_ptr(),
         odt, _ptr(lse), num_splits, workspace.data_ptr(),
         workspace.numel(), _stream()))
+    return (out, lse) if return_lse else out
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # the library's static decode scratch per GPU
+
+
+def decode_noalloc(cache: NVFP4KVCache, q: torch.Tensor, kv_lens: torch.Tensor,
+                   block_table: torch.Tensor, max_kv_len: int, sm_scale: float,
+                   out: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                   return_lse: bool = False, num_splits: int = 0):
+    """paged_decode_nvfp4_noalloc: ``decode`` without a workspace (the library's static
+    per-GPU scratch holds the partials; calls on one GPU must not overlap).  ``out`` and ``lse``
+    are allocated here only when the caller passes none."""
+    odt = _attn_out_code(out_dtype if out is None else out.dtype)
+    _need(q, torch.bfloat16, "q"); _need(kv_lens, torch.int32, "kv_lens")
+    _need(block_table, torch.int32, "block_table")
+    if not q.is_contiguous() or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError("q and block_table must be contiguous (block_table [batch][stride])")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [batch][Hq][{HEAD_DIM}], got {tuple(q.shape)}")
+    batch, hq = q.shape[0], q.shape[1]
+    if kv_lens.numel() != batch or block_table.shape[0] != batch:
+        raise ValueError(f"kv_lens and block_table must have one entry / row per sequence ({batch})")
+    if out is None:
+        out = torch.empty((batch, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    _check_out(out, batch, hq, q.device)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    d = cache.desc()
+    _check(load_library().paged_decode_nvfp4_noalloc(
+        ctypes.byref(d), q.data_ptr(), kv_lens.data_ptr(), block_table.data_ptr(),
+        block_table.shape[1], batch, max_kv_len, hq, sm_scale, out.data_ptr(), odt, _ptr(lse),
+        num_splits, _stream()))
     return (out, lse) if return_lse else out

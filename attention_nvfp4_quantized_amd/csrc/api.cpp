@@ -126,6 +126,88 @@ int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, in
 
 bool group_ok(int g) { return g >= 1 && g <= 64 && (256 % g) == 0; }
 
+// Decode arguments checked and turned into kernel parameters; the workspace pointers are filled
+// by launch_decode_plan.
+struct DecodePlan {
+  nvfp4kv::DecodeParams p;
+  nvfp4kv::MergeParams m;
+  size_t workspace_bytes;
+};
+
+int plan_decode(const nvfp4kv_cache_t* cache, const void* q, const int32_t* kv_lens,
+                const int32_t* block_table, int32_t block_table_stride, int32_t batch,
+                int32_t max_kv_len, int32_t num_qo_heads, float sm_scale, void* out,
+                int32_t out_dtype, float* lse, int32_t num_splits, DecodePlan* plan) {
+  if (int e = check_cache(cache)) return e;
+  if (int e = check_not_f16(cache, "paged_decode_nvfp4")) return e;
+  if (batch < 0 || max_kv_len < 0) return fail(NVFP4KV_EINVAL, "negative size");
+  if (batch == 0) return ok();
+  if (!q || !kv_lens || !block_table || !out)
+    return fail(NVFP4KV_EINVAL, "q, kv_lens, block_table or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4KV_EINVAL, "q/out must be 16-byte aligned");
+  if (num_qo_heads < 1 || num_qo_heads % cache->num_kv_heads)
+    return fail(NVFP4KV_EINVAL, "num_qo_heads %d is not a multiple of num_kv_heads %d", num_qo_heads,
+                cache->num_kv_heads);
+  const int g = num_qo_heads / cache->num_kv_heads;
+  if (g > 16) return fail(NVFP4KV_EUNSUPPORTED, "decode supports query groups of at most 16 (got %d)", g);
+  if ((long)batch * num_qo_heads > (1L << 30))
+    return fail(NVFP4KV_EINVAL, "batch x num_qo_heads = %ld rows: too large for one launch",
+                (long)batch * num_qo_heads);
+  if (max_kv_len < 1) return fail(NVFP4KV_EINVAL, "max_kv_len must be >= 1");
+  if (block_table_stride < (max_kv_len + 15) / 16)
+    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
+                block_table_stride, max_kv_len);
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "sm_scale must be > 0");
+  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32)
+    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
+  if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
+  int chunk = 0;
+  const int s = decode_splits(batch, cache->num_kv_heads, max_kv_len, num_splits, &chunk);
+  const long items = (long)cache->num_kv_heads * batch * s;
+  if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
+
+  nvfp4kv::DecodeParams& p = plan->p;
+  p = nvfp4kv::DecodeParams{};
+  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
+  p.k_data = cache->k_data;
+  p.k_scale = cache->k_scale;
+  p.v_data = cache->v_data;
+  p.v_scale = cache->v_scale;
+  p.q = (const uint16_t*)q;
+  p.kv_lens = kv_lens;
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.batch = batch;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_qo_heads = num_qo_heads;
+  p.group = g;
+  p.num_splits = s;
+  p.chunk = chunk;
+  p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
+  nvfp4kv::MergeParams& m = plan->m;
+  m = nvfp4kv::MergeParams{};
+  m.num_splits = s;
+  m.rows = batch * num_qo_heads;
+  m.out_scale = cache->v_global;
+  m.out = out;
+  m.out_f32 = out_dtype == NVFP4KV_OUT_F32;
+  m.lse = lse;
+  plan->workspace_bytes = (size_t)s * batch * num_qo_heads * kPartRowBytes;
+  return NVFP4KV_OK;
+}
+
+// Launch the split kernel and the merge with the partials in `ws` (fp16 partials, then the
+// float32 log-sum-exps).
+int launch_decode_plan(DecodePlan& plan, void* ws, hipStream_t st) {
+  plan.p.part_o = (uint16_t*)ws;
+  plan.p.part_lse = (float*)(plan.p.part_o + (size_t)plan.p.num_splits * plan.p.batch *
+                                                 plan.p.num_qo_heads * 128);
+  plan.m.part_o = plan.p.part_o;
+  plan.m.part_lse = plan.p.part_lse;
+  if (int e = check_launch(nvfp4kv::launch_decode(plan.p, st), "decode launch")) return e;
+  return check_launch(nvfp4kv::launch_merge(plan.m, st), "merge launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,70 +434,40 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
                        int32_t max_kv_len, int32_t num_qo_heads, float sm_scale, void* out,
                        int32_t out_dtype, float* lse, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  if (int e = check_cache(cache)) return e;
-  if (int e = check_not_f16(cache, "paged_decode_nvfp4")) return e;
-  if (batch < 0 || max_kv_len < 0) return fail(NVFP4KV_EINVAL, "negative size");
+  DecodePlan plan;
+  if (int e = plan_decode(cache, q, kv_lens, block_table, block_table_stride, batch, max_kv_len,
+                          num_qo_heads, sm_scale, out, out_dtype, lse, num_splits, &plan))
+    return e;
   if (batch == 0) return ok();
-  if (!q || !kv_lens || !block_table || !out)
-    return fail(NVFP4KV_EINVAL, "q, kv_lens, block_table or out is NULL");
-  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4KV_EINVAL, "q/out must be 16-byte aligned");
-  if (num_qo_heads < 1 || num_qo_heads % cache->num_kv_heads)
-    return fail(NVFP4KV_EINVAL, "num_qo_heads %d is not a multiple of num_kv_heads %d", num_qo_heads,
-                cache->num_kv_heads);
-  const int g = num_qo_heads / cache->num_kv_heads;
-  if (g > 16) return fail(NVFP4KV_EUNSUPPORTED, "decode supports query groups of at most 16 (got %d)", g);
-  if ((long)batch * num_qo_heads > (1L << 30))
-    return fail(NVFP4KV_EINVAL, "batch x num_qo_heads = %ld rows: too large for one launch",
-                (long)batch * num_qo_heads);
-  if (max_kv_len < 1) return fail(NVFP4KV_EINVAL, "max_kv_len must be >= 1");
-  if (block_table_stride < (max_kv_len + 15) / 16)
-    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
-                block_table_stride, max_kv_len);
-  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "sm_scale must be > 0");
-  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32)
-    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
-  if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
-  int chunk = 0;
-  const int s = decode_splits(batch, cache->num_kv_heads, max_kv_len, num_splits, &chunk);
-  const long items = (long)cache->num_kv_heads * batch * s;
-  if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
-  const size_t need = (size_t)s * batch * num_qo_heads * kPartRowBytes;
-  if (!workspace || workspace_bytes < need)
-    return fail(NVFP4KV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+  if (!workspace || workspace_bytes < plan.workspace_bytes)
+    return fail(NVFP4KV_EWORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
+  return launch_decode_plan(plan, workspace, (hipStream_t)stream);
+}
 
-  nvfp4kv::DecodeParams p{};
-  p.fp8 = cache->kv_format == NVFP4KV_FORMAT_FP8;
-  p.k_data = cache->k_data;
-  p.k_scale = cache->k_scale;
-  p.v_data = cache->v_data;
-  p.v_scale = cache->v_scale;
-  p.q = (const uint16_t*)q;
-  p.kv_lens = kv_lens;
-  p.block_table = block_table;
-  p.bt_stride = block_table_stride;
-  p.batch = batch;
-  p.num_kv_heads = cache->num_kv_heads;
-  p.num_qo_heads = num_qo_heads;
-  p.group = g;
-  p.num_splits = s;
-  p.chunk = chunk;
-  p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
-  p.part_o = (uint16_t*)workspace;
-  p.part_lse = (float*)(p.part_o + (size_t)s * batch * num_qo_heads * 128);
-  hipStream_t st = (hipStream_t)stream;
-  if (int e = check_launch(nvfp4kv::launch_decode(p, st), "decode launch")) return e;
-  nvfp4kv::MergeParams m{};
-  m.part_o = p.part_o;
-  m.part_lse = p.part_lse;
-  m.num_splits = s;
-  m.rows = batch * num_qo_heads;
-  m.out_scale = cache->v_global;
-  m.out = out;
-  m.out_f32 = out_dtype == NVFP4KV_OUT_F32;
-  m.lse = lse;
-  return check_launch(nvfp4kv::launch_merge(m, st), "merge launch");
+int paged_decode_nvfp4_noalloc(const nvfp4kv_cache_t* cache, const void* q,
+                               const int32_t* kv_lens, const int32_t* block_table,
+                               int32_t block_table_stride, int32_t batch, int32_t max_kv_len,
+                               int32_t num_qo_heads, float sm_scale, void* out, int32_t out_dtype,
+                               float* lse, int32_t num_splits, void* stream) {
+  DecodePlan plan;
+  if (int e = plan_decode(cache, q, kv_lens, block_table, block_table_stride, batch, max_kv_len,
+                          num_qo_heads, sm_scale, out, out_dtype, lse, num_splits, &plan))
+    return e;
+  if (batch == 0) return ok();
+  if (plan.workspace_bytes > nvfp4kv::kDecodeScratchBytes)
+    return fail(NVFP4KV_EWORKSPACE,
+                "decode of %d sequences x %d query heads in %d key splits needs %zu scratch bytes; "
+                "the allocation-free entry point holds %zu per GPU (call paged_decode_nvfp4 with a "
+                "workspace)",
+                batch, num_qo_heads, plan.p.num_splits, plan.workspace_bytes,
+                nvfp4kv::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (hipError_t e = nvfp4kv::decode_scratch(&scratch, &scratch_bytes); e != hipSuccess)
+    return fail(NVFP4KV_EHIP, "static decode scratch lookup: %s", hipGetErrorString(e));
+  return launch_decode_plan(plan, scratch, (hipStream_t)stream);
 }
 
 }  // extern "C"

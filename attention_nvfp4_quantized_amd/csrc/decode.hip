@@ -25,6 +25,8 @@
 //    groups before it run without any per-token range selects or score masks.
 //  * The same kernel reads the FP8 (E4M3FN) control cache (FMT = 1): 32 bytes per lane and
 //    token, one conversion per pair of values and no block scales.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernel_params.hpp"
 
@@ -363,6 +365,36 @@ __global__ __launch_bounds__(256, DecodeShape<FMT>::kBlocks) void nvfp4_decode_k
     p.part_o[(prow0 + c) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(L > 0.0f ? o / L : 0.0f));
     if (d == 0) p.part_lse[prow0 + c] = L > 0.0f ? M + __log2f(L) : kNegInf;
   }
+}
+
+// ---- static scratch of the allocation-free decode entry point ----------------------------
+// One array per GPU, held from code-object load until the process ends.  Host code never uses
+// the array's name as an address (on the host it names a stand-in, not device memory): the
+// device address of the current GPU's copy comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and is what the kernels receive.  The decode writes every
+// partial and log-sum-exp the merge uses before the merge reads it, so nothing in the array
+// has to start at zero; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = addr;
+  }
+  *ptr = per_device[dev];
+  *bytes = kDecodeScratchBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

@@ -115,6 +115,13 @@ struct DecodeParams {
   int32_t fp8;            // FP8 E4M3FN cache (else NVFP4)
 };
 
+// Static device scratch of the allocation-free decode entry point (bytes per GPU).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+
+// Address of this GPU's copy of the static decode scratch (the current device's), looked up
+// once per device; *bytes receives its size.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
+
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 hipError_t launch_repack(const RepackParams& p, int batch, int max_pages, hipStream_t stream);

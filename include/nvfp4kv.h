@@ -28,8 +28,9 @@
  *     host pointer to a descriptor holding device pointers.  `stream` is a hipStream_t (NULL =
  *     the default stream).  Calls are asynchronous on `stream`.
  *   - The library never allocates, frees or synchronizes.  Entry points that need scratch memory
- *     take a caller-provided workspace and report its size through a *_workspace_size call.
- *   - Only the cache (append), `out`, `lse` and `workspace` are written.
+ *     take a caller-provided workspace and report its size through a *_workspace_size call;
+ *     paged_decode_nvfp4_noalloc uses a static device array of the library instead.
+ *   - Only the cache (append), `out`, `lse` and `workspace` (or that static array) are written.
  *   - Return value: 0 on success, otherwise a negative NVFP4KV_E* code; the message of the last
  *     failure on the calling thread is returned by nvfp4kv_last_error().  Unsupported shapes are
  *     rejected; there is no fallback path.
@@ -194,6 +195,28 @@ int paged_decode_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_
                        int32_t max_kv_len, int32_t num_qo_heads, float sm_scale, void* out,
                        int32_t out_dtype, float* lse, int32_t num_splits, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate or hand over scratch memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  The same
+ * computation, kernels and results as paged_decode_nvfp4 (same arguments without the workspace);
+ * the split partials go to a static device array of NVFP4KV_DECODE_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  Nothing is allocated or freed:
+ * the array's device address is looked up on the first call on each device.
+ *   - A call whose partials need more than NVFP4KV_DECODE_SCRATCH_BYTES (split count x batch x
+ *     num_qo_heads x 260 bytes, as paged_decode_nvfp4_workspace_size reports) is rejected with
+ *     NVFP4KV_EWORKSPACE before any device work.
+ *   - Every call on a GPU uses that GPU's one array, which keeps the last call's contents
+ *     (nothing in it has to start at zero).  Calls that overlap on one GPU (different streams
+ *     or host threads, or in flight at the same time) race on the array: order them, e.g. on one
+ *     stream.
+ */
+#define NVFP4KV_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int paged_decode_nvfp4_noalloc(const nvfp4kv_cache_t* cache, const void* q,
+                               const int32_t* kv_lens, const int32_t* block_table,
+                               int32_t block_table_stride, int32_t batch, int32_t max_kv_len,
+                               int32_t num_qo_heads, float sm_scale, void* out, int32_t out_dtype,
+                               float* lse, int32_t num_splits, void* stream);
 
 /* Message describing the last non-zero return on the calling thread ("" if none). */
 const char* nvfp4kv_last_error(void);

@@ -231,3 +231,27 @@ def test_binding_rejects_fp16_attention_output():
             fn(*args, out=torch.empty((1, 1, 128), dtype=torch.float16))
         with pytest.raises(TypeError, match="bfloat16 or float32"):
             fn(*args, out_dtype=torch.int32)
+
+
+def test_noalloc_decode_rejects_more_than_its_scratch():
+    """The allocation-free decode refuses, before any device call, a problem whose partials pass
+    its static scratch (here 16 splits x 4096 sequences x 32 heads x 260 B), and names both sizes;
+    argument errors come first, as in paged_decode_nvfp4."""
+    lib = load_library()
+    d = _desc()
+
+    def dec(**kw):
+        a = dict(q=16, kv=16, bt=16, bts=8192, batch=4096, max_kv=131072, hq=32, sm=0.088, out=16,
+                 odt=0, lse=None, splits=0)
+        a.update(kw)
+        return lib.paged_decode_nvfp4_noalloc(ctypes.byref(d), a["q"], a["kv"], a["bt"], a["bts"],
+                                              a["batch"], a["max_kv"], a["hq"], a["sm"], a["out"],
+                                              a["odt"], a["lse"], a["splits"], None)
+    need = A.decode_workspace_size(4096, 131072, 32, 8)
+    assert need > A.DECODE_SCRATCH_BYTES
+    assert dec() == -3
+    msg = _err()
+    assert str(need) in msg and str(A.DECODE_SCRATCH_BYTES) in msg
+    assert dec(q=None) == -1
+    assert dec(hq=8 * 32) == -2
+    assert dec(batch=0) == 0 and _err() == ""
