@@ -156,6 +156,8 @@ def _nvfp4_row_brute(row):
 def _quantize_brute(row, scheme):
     if scheme == "mxfp4":
         return [v for j in range(0, len(row), 32) for v in _mx_block_brute(row[j:j + 32])]
+    if scheme == "mxfp8":
+        return [v for j in range(0, len(row), 32) for v in _mx8_block_brute(row[j:j + 32])]
     if scheme == "nvfp4":
         return _nvfp4_row_brute(row)
     return pins.expected_nvfp4_dual_row(row)
@@ -238,3 +240,212 @@ def test_pins_catch_dual_level_without_the_448():
     import types
     with pytest.raises(AssertionError):
         pins.check_nvfp4_dual(types.SimpleNamespace(quantize_q=bad))
+
+
+# ---- MXFP8 queries and the two-term E4M3 bridge of K (the GPU A4Q variant's scheme) --------
+
+E4M3_POS = [f for f in pins._fraction_e4m3_table()]
+
+
+def _mx8_block_brute(vals):
+    """MXFP8 of one 32-value block by exhaustive search over the E4M3 values: X = 2^(e - 8)
+    with e the integer 2^e <= amax < 2^(e+1); |v| / X goes to the nearest E4M3 magnitude (ties:
+    the even code), beyond 448 to 448; sign kept."""
+    fr = [Fraction(float(v)) for v in vals]
+    amax = max(abs(v) for v in fr)
+    if amax == 0:
+        return [0.0] * len(vals)
+    e = 0
+    while Fraction(2) ** e > amax:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= amax:
+        e += 1
+    X = Fraction(2) ** (e - 8)
+    out = []
+    for v in fr:
+        r = abs(v) / X
+        if r >= E4M3_POS[-1]:
+            mag = E4M3_POS[-1]
+        else:
+            best = None
+            for code, gv in enumerate(E4M3_POS):
+                d = abs(r - gv)
+                if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+                    best = (d, code, gv)
+            mag = best[2]
+        out.append(float((-1 if v < 0 else 1) * mag * X))
+    return out
+
+
+def test_mxfp8_against_exhaustive_search():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((60, 64)) * np.exp(rng.uniform(-12, 12, (60, 1)))
+    x[3, :32] = 0.0
+    x[4, 5] = 2.0 ** 7 * 1.9375  # amax / X = 496: saturates to 448
+    x[5, 9] = 512.0              # amax a power of two
+    x = x.astype(np.float32).astype(np.float64)
+    got = a4q.mxfp8_values(x)
+    for i in range(x.shape[0]):
+        for j in (0, 32):
+            assert list(got[i, j:j + 32]) == _mx8_block_brute(x[i, j:j + 32]), (i, j)
+
+
+def test_pins_catch_mxfp8_without_saturation_bound():
+    def bad(x):  # X one exponent higher (amax / X in [128, 256)): no saturation, other codes
+        x = np.asarray(x, np.float64)
+        _, ex = np.frexp(np.abs(x).max())
+        X = 2.0 ** (ex - 8)
+        return codec.e4m3_value(codec.e4m3_encode_signed(x / X)) * X
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((4, 32))
+    x[:, 0] = 1.9 * np.exp2(np.arange(4))  # amax / X = 486.4 under the rule: saturates to 448
+    with pytest.raises(AssertionError):
+        for i in range(4):
+            assert list(bad(x[i])) == _mx8_block_brute(x[i])
+
+
+def _bridge_brute(x_block, s_pair):
+    """The two-term bridge of one 32-value block by exact rationals: E from the larger scale,
+    X = 2^(E - 5); hi, lo nearest-even E4M3 (searched exhaustively) of y and y - hi."""
+    def fl(sv):
+        if sv == 0:
+            return -15
+        e = 0
+        while Fraction(2) ** e > sv:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= sv:
+            e += 1
+        return e
+    X = Fraction(2) ** (max(fl(Fraction(float(s_pair[0]))), fl(Fraction(float(s_pair[1])))) - 5)
+
+    def near(r):
+        a = abs(r)
+        best = None
+        for code, gv in enumerate(E4M3_POS):
+            d = abs(a - gv)
+            if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+                best = (d, gv)
+        return (-1 if r < 0 else 1) * best[1]
+    out = []
+    for v in x_block:
+        y = Fraction(float(v)) / X
+        hi = near(y)
+        lo = near(y - hi)
+        out.append(float(X * (hi + lo)))
+    return out
+
+
+def _cache_blocks(seed, n, ratio_exp):
+    """NVFP4 cache values of n 32-value blocks whose two 16-value halves differ in scale by up
+    to 2^ratio_exp (both halves inside the E4M3 scale range), with their block scales."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 32)) * np.exp2(rng.uniform(-8 + ratio_exp / 2, 8 - ratio_exp / 2, (n, 1)))
+    x[:, 16:] *= np.exp2(-rng.integers(0, ratio_exp + 1, (n, 1)))
+    codes, sc = codec.quantize(x.astype(np.float32))
+    return codec.dequantize(codec.pack(codes), sc), codec.e4m3_value(sc)
+
+
+def test_k_bridge_is_exact_within_a_scale_ratio_of_2_to_the_8():
+    xv, s = _cache_blocks(43, 3000, 8)
+    hi, lo, e, br = a4q.k_bridge(xv, s)
+    assert np.array_equal(br, xv)
+    y = xv / np.repeat(np.exp2(e), 32, axis=-1)
+    assert np.abs(y).max() < 384
+
+
+def test_k_bridge_against_exact_rationals_on_wide_blocks():
+    # first halves' scales near 2^7.4, second halves' 2^-3.3 .. 2^-7.3: 2^11 .. 2^15 apart, so
+    # the low term of the small half is not always exact
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((60, 32))
+    x[:, :16] *= 400.0
+    x[:, 16:] *= np.exp2(-rng.uniform(2, 6, (60, 1)))
+    codes, sc = codec.quantize(x.astype(np.float32))
+    xv, s = codec.dequantize(codec.pack(codes), sc), codec.e4m3_value(sc)
+    assert np.all(s > 0)
+    _, _, _, br = a4q.k_bridge(xv, s)
+    for i in range(xv.shape[0]):
+        assert list(br[i]) == _bridge_brute(xv[i], s[i]), i
+    assert not np.array_equal(br, xv)  # some values were rounded by the bridge
+
+
+def test_pins_catch_k_bridge_without_the_low_term():
+    def bad(x, s):
+        hi, lo, e, br = a4q.k_bridge(x, s)
+        X = np.repeat(np.exp2(e), 32, axis=-1)
+        return hi, lo, e, X * codec.e4m3_value(hi)
+    xv, s = _cache_blocks(45, 200, 4)
+    with pytest.raises(AssertionError):
+        assert np.array_equal(bad(xv, s)[3], xv)
+
+
+def check_prefill_mx_paged(prefill_mx, q_format, seed=27):
+    """prefill_mx on a paged, ragged, GQA, causal batch against Python loops: queries quantized
+    by the exhaustive MX searches above, K bridged by exact rationals from independently
+    quantized values, softmax and PV in Python floats."""
+    rng = np.random.default_rng(seed)
+    d, hq, hkv, ps = 64, 4, 2, 16
+    q_lens, kv_lens = [3, 1, 4], [19, 5, 33]
+    pages = [(n + ps - 1) // ps for n in kv_lens]
+    perm = rng.permutation(sum(pages) + 2)
+    bt = np.zeros((3, max(pages)), np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[off:off + n]; off += n
+    oc = cache.PagedCache(sum(pages) + 2, hkv, head_dim=d, page_size=ps)
+    sm = 1 / math.sqrt(d)
+    kd, vd, qs = [], [], []
+    table = pins._fraction_e4m3_table()
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        k = (rng.standard_normal((kl, hkv, d)) * 2).astype(np.float32)
+        k[:, :, :16] *= 8  # the first 16-value block of every K row x8
+        v = rng.standard_normal((kl, hkv, d)).astype(np.float32)
+        kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+        vb = (v.view(np.uint32) >> 16).astype(np.uint16)
+        pos = np.arange(kl)
+        oc.append(kb, vb, bt[b][pos // ps].astype(np.int64) * ps + pos % ps)
+        kk = np.zeros((kl, hkv, d))
+        for t in range(kl):
+            for h in range(hkv):
+                row = pins.bf16_value(kb[t, h])
+                vals, scs = [], []
+                for b0 in range(0, d, 16):
+                    sc, codes = pins.expected_block(row[b0:b0 + 16], Fraction(1), table)
+                    scs.append(float(table[sc]))
+                    vals += [float((-1 if c & 8 else 1) * GRID[c & 7] * table[sc]) for c in codes]
+                for j in range(0, d, 32):
+                    kk[t, h, j:j + 32] = _bridge_brute(vals[j:j + 32], scs[j // 16:j // 16 + 2])
+        kd.append(kk)
+        vd.append(np.array([_nvfp4_row_brute(pins.bf16_value(r)) for r in vb.reshape(-1, d)]).reshape(kl, hkv, d))
+        qs.append((rng.standard_normal((ql, hq, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    qb = np.concatenate(qs)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    got = prefill_mx(oc, qb, cu, kv_lens, bt, sm, q_format)
+    quant = _mx8_block_brute if q_format == "mxfp8" else _mx_block_brute
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        for h in range(hq):
+            kvh = h // (hq // hkv)
+            for i in range(ql):
+                row = pins.bf16_value(qs[b][i, h])
+                qv = [v for j in range(0, d, 32) for v in quant(row[j:j + 32])]
+                last = kl - ql + i
+                z = [sm * math.fsum(qv[t] * kd[b][j, kvh, t] for t in range(d)) for j in range(last + 1)]
+                zm = max(z)
+                p = [math.exp(x - zm) for x in z]
+                den = math.fsum(p)
+                for t in range(d):
+                    ref = math.fsum(p[j] * vd[b][j, kvh, t] for j in range(len(p))) / den
+                    assert abs(got[cu[b] + i, h, t] - ref) < 1e-12, (q_format, b, h, i, t)
+
+
+@pytest.mark.parametrize("q_format", ["mxfp8", "mxfp4"])
+def test_prefill_mx_paged_ragged_vs_brute_force(q_format):
+    check_prefill_mx_paged(a4q.prefill_mx, q_format)
+
+
+def test_pins_catch_prefill_mx_with_unbridged_queries():
+    def bad(oc, qb, cu, kv_lens, bt, sm, q_format):  # queries left unquantized
+        from oracle import attention
+        return attention.prefill(oc, qb, cu, kv_lens, bt, sm)[0]
+    with pytest.raises(AssertionError):
+        check_prefill_mx_paged(bad, "mxfp8")
