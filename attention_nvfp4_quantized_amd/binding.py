@@ -63,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_decode_nvfp4_workspace_size.restype = SZ
     lib.paged_decode_nvfp4.argtypes = [C, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P, SZ, P]
     lib.paged_decode_nvfp4.restype = ctypes.c_int
+    lib.paged_prefill_nvfp4_a4q_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
+    lib.paged_prefill_nvfp4_a4q_workspace_size.restype = SZ
+    lib.paged_prefill_nvfp4_a4q.argtypes = [C, P, P, P, P, I32, I32, I32, I32, I32, I32, F, I32, P,
+                                            I32, P, I32, I32, P, SZ, P]
+    lib.paged_prefill_nvfp4_a4q.restype = ctypes.c_int
     lib.paged_decode_nvfp4_noalloc.argtypes = [C, P, P, P, I32, I32, I32, I32, F, P, I32, P, I32, P]
     lib.paged_decode_nvfp4_noalloc.restype = ctypes.c_int
     lib.nvfp4kv_last_error.argtypes = []
@@ -243,6 +248,53 @@ def prefill(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
         block_table.data_ptr(), block_table.shape[1], batch, total_q, max_q_len, max_kv_len, hq,
         sm_scale, 1 if causal else 0, out.data_ptr(), odt,
         _ptr(lse), num_splits, _ptr(workspace) if ws_bytes else None, ws_bytes, _stream()))
+    return (out, lse) if return_lse else out
+
+
+_A4Q_FORMATS = {"mxfp8": 0, "mxfp4": 1}
+
+
+def prefill_a4q_workspace_size(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,
+                               num_splits=0) -> int:
+    return load_library().paged_prefill_nvfp4_a4q_workspace_size(
+        batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads, HEAD_DIM, num_splits)
+
+
+def prefill_a4q(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                kv_lens: torch.Tensor, block_table: torch.Tensor, max_q_len: int, max_kv_len: int,
+                sm_scale: float, q_format: str = "mxfp8", causal: bool = True,
+                out: torch.Tensor | None = None, out_dtype=torch.bfloat16, return_lse: bool = False,
+                num_splits: int = 0, workspace: torch.Tensor | None = None):
+    """paged_prefill_nvfp4_a4q: ``prefill`` with the query quantized in the kernel to MX blocks
+    (q_format "mxfp8" or "mxfp4") and QK on gfx950's block-scaled MFMA; NVFP4 caches only."""
+    if q_format not in _A4Q_FORMATS:
+        raise ValueError(f"q_format must be one of {sorted(_A4Q_FORMATS)}, got {q_format!r}")
+    odt = _attn_out_code(out_dtype if out is None else out.dtype)
+    _need(q, torch.bfloat16, "q"); _need(cu_seqlens_q, torch.int32, "cu_seqlens_q")
+    _need(kv_lens, torch.int32, "kv_lens"); _need(block_table, torch.int32, "block_table")
+    if not q.is_contiguous() or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError("q and block_table must be contiguous (block_table [batch][stride])")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [total_q][Hq][{HEAD_DIM}], got {tuple(q.shape)}")
+    total_q, hq = q.shape[0], q.shape[1]
+    batch = kv_lens.numel()
+    if cu_seqlens_q.numel() != batch + 1 or block_table.shape[0] != batch:
+        raise ValueError(f"cu_seqlens_q must hold batch + 1 = {batch + 1} offsets and "
+                         f"block_table {batch} rows (one per kv_lens entry)")
+    if out is None:
+        out = torch.empty((total_q, hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    _check_out(out, total_q, hq, q.device)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    ws_bytes = prefill_a4q_workspace_size(batch, total_q, max_q_len, max_kv_len, hq,
+                                          cache.num_kv_heads, num_splits)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    d = cache.desc()
+    _check(load_library().paged_prefill_nvfp4_a4q(
+        ctypes.byref(d), q.data_ptr(), cu_seqlens_q.data_ptr(), kv_lens.data_ptr(),
+        block_table.data_ptr(), block_table.shape[1], batch, total_q, max_q_len, max_kv_len, hq,
+        sm_scale, 1 if causal else 0, out.data_ptr(), odt, _ptr(lse), _A4Q_FORMATS[q_format],
+        num_splits, _ptr(workspace) if ws_bytes else None, ws_bytes, _stream()))
     return (out, lse) if return_lse else out
 
 

@@ -126,6 +126,139 @@ int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, in
 
 bool group_ok(int g) { return g >= 1 && g <= 64 && (256 % g) == 0; }
 
+// Prefill arguments checked and turned into kernel parameters (a8 = the A4Q-style kernel, which
+// always runs the 8-wave kernel); the workspace pointers are filled by launch_prefill_plan.
+struct PrefillPlan {
+  nvfp4kv::PrefillParams p;
+  int nw;
+  bool empty;
+  size_t workspace_bytes;
+  void* out;
+  float* lse;
+};
+
+size_t prefill_workspace(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t num_splits, bool a4q) {
+  if (batch <= 0 || total_q <= 0 || max_q_len <= 0 || num_kv_heads <= 0 || num_qo_heads <= 0 ||
+      head_dim != 128 || num_qo_heads % num_kv_heads)
+    return 0;
+  const int g = num_qo_heads / num_kv_heads;
+  if (!group_ok(g)) return 0;
+  const int nw = a4q ? 8 : prefill_waves(max_q_len, g);
+  const int q_tiles = (max_q_len + (32 * nw / g) - 1) / (32 * nw / g);
+  const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, nw, num_splits);
+  if (s <= 1) return 0;
+  return (size_t)s * total_q * num_qo_heads * kPartRowBytes;
+}
+
+int plan_prefill(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_seqlens_q,
+                 const int32_t* kv_lens, const int32_t* block_table, int32_t block_table_stride,
+                 int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                 int32_t num_qo_heads, float sm_scale, int32_t causal, void* out, int32_t out_dtype,
+                 float* lse, int32_t num_splits, bool a4q, PrefillPlan* plan) {
+  plan->empty = false;
+  if (int e = check_cache(cache)) return e;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0)
+    return fail(NVFP4KV_EINVAL, "negative size");
+  if (batch == 0 || total_q == 0 || max_q_len == 0) {
+    plan->empty = true;
+    return ok();
+  }
+  if (!q || !cu_seqlens_q || !kv_lens || !block_table || !out)
+    return fail(NVFP4KV_EINVAL, "q, cu_seqlens_q, kv_lens, block_table or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4KV_EINVAL, "q/out must be 16-byte aligned");
+  if (num_qo_heads < 1 || num_qo_heads % cache->num_kv_heads)
+    return fail(NVFP4KV_EINVAL, "num_qo_heads %d is not a multiple of num_kv_heads %d", num_qo_heads,
+                cache->num_kv_heads);
+  const int g = num_qo_heads / cache->num_kv_heads;
+  if (!group_ok(g)) return fail(NVFP4KV_EUNSUPPORTED, "query group size %d unsupported", g);
+  // output rows (token, head) are indexed in 32 bits, with room for the merge grid's rounding
+  if ((long)total_q * num_qo_heads > (1L << 30))
+    return fail(NVFP4KV_EINVAL, "total_q x num_qo_heads = %ld rows: too large for one launch",
+                (long)total_q * num_qo_heads);
+  if (block_table_stride < (max_kv_len + 15) / 16)
+    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
+                block_table_stride, max_kv_len);
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "sm_scale must be > 0");
+  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32)
+    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
+  if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
+
+  const int nw = a4q ? 8 : prefill_waves(max_q_len, g);
+  const int rows = 32 * nw / g;
+  const int q_tiles = (max_q_len + rows - 1) / rows;
+  const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);
+  const long items = (long)cache->num_kv_heads * batch * q_tiles * s;
+  if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
+
+  nvfp4kv::PrefillParams& p = plan->p;
+  p = nvfp4kv::PrefillParams{};
+  p.format = cache->kv_format;
+  p.k_data = cache->k_data;
+  p.k_scale = cache->k_scale;
+  p.v_data = cache->v_data;
+  p.v_scale = cache->v_scale;
+  p.q = (const uint16_t*)q;
+  p.cu_q = cu_seqlens_q;
+  p.kv_lens = kv_lens;
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.batch = batch;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.num_qo_heads = num_qo_heads;
+  p.group = g;
+  p.q_tiles = q_tiles;
+  p.num_splits = s;
+  p.causal = causal ? 1 : 0;
+  p.total_q = total_q;
+  p.total_items = (int)items;
+  p.items_per_xcd = (int)((items + 7) / 8);
+  p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
+  p.out_scale = cache->v_global;
+  p.out_f32 = out_dtype == NVFP4KV_OUT_F32;
+  plan->nw = nw;
+  plan->out = out;
+  plan->lse = lse;
+  plan->workspace_bytes = s > 1 ? (size_t)s * total_q * num_qo_heads * kPartRowBytes : 0;
+  return NVFP4KV_OK;
+}
+
+// Launch the prefill (stock kernels for q_format < 0, else the A4Q-style kernel) and, with key
+// splits, the merge of the partials kept in `ws`.
+int launch_prefill_plan(PrefillPlan& plan, void* workspace, size_t workspace_bytes, int q_format,
+                        hipStream_t st) {
+  nvfp4kv::PrefillParams& p = plan.p;
+  auto launch = [&]() {
+    return q_format < 0 ? nvfp4kv::launch_prefill(p, plan.nw, st)
+                        : nvfp4kv::launch_prefill_a4q(p, q_format, st);
+  };
+  if (p.num_splits > 1) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+      return fail(NVFP4KV_EWORKSPACE, "prefill needs %zu workspace bytes, got %zu", plan.workspace_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
+    p.part_o = (uint16_t*)workspace;
+    p.part_lse = (float*)(p.part_o + (size_t)p.num_splits * p.total_q * p.num_qo_heads * 128);
+    p.lse = nullptr;
+    p.out = nullptr;
+    if (int e = check_launch(launch(), "prefill launch")) return e;
+    nvfp4kv::MergeParams m{};
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.num_splits = p.num_splits;
+    m.rows = p.total_q * p.num_qo_heads;
+    m.out_scale = p.out_scale;
+    m.out = plan.out;
+    m.out_f32 = p.out_f32;
+    m.lse = plan.lse;
+    return check_launch(nvfp4kv::launch_merge(m, st), "merge launch");
+  }
+  p.lse = plan.lse;
+  p.out = plan.out;
+  return check_launch(launch(), "prefill launch");
+}
+
 // Decode arguments checked and turned into kernel parameters; the workspace pointers are filled
 // by launch_decode_plan.
 struct DecodePlan {
@@ -317,16 +450,16 @@ size_t paged_prefill_nvfp4_workspace_size(int32_t batch, int32_t total_q, int32_
                                           int32_t max_kv_len, int32_t num_qo_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t num_splits) {
-  if (batch <= 0 || total_q <= 0 || max_q_len <= 0 || num_kv_heads <= 0 || num_qo_heads <= 0 ||
-      head_dim != 128 || num_qo_heads % num_kv_heads)
-    return 0;
-  const int g = num_qo_heads / num_kv_heads;
-  if (!group_ok(g)) return 0;
-  const int nw = prefill_waves(max_q_len, g);
-  const int q_tiles = (max_q_len + (32 * nw / g) - 1) / (32 * nw / g);
-  const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, nw, num_splits);
-  if (s <= 1) return 0;
-  return (size_t)s * total_q * num_qo_heads * kPartRowBytes;
+  return prefill_workspace(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,
+                           head_dim, num_splits, false);
+}
+
+size_t paged_prefill_nvfp4_a4q_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
+                                              int32_t max_kv_len, int32_t num_qo_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t num_splits) {
+  return prefill_workspace(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,
+                           head_dim, num_splits, true);
 }
 
 int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_seqlens_q,
@@ -336,87 +469,34 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
                         float sm_scale, int32_t causal, void* out, int32_t out_dtype, float* lse,
                         int32_t num_splits, void* workspace, size_t workspace_bytes,
                         void* stream) {
+  PrefillPlan plan;
+  if (int e = plan_prefill(cache, q, cu_seqlens_q, kv_lens, block_table, block_table_stride, batch,
+                           total_q, max_q_len, max_kv_len, num_qo_heads, sm_scale, causal, out,
+                           out_dtype, lse, num_splits, false, &plan))
+    return e;
+  if (plan.empty) return ok();
+  return launch_prefill_plan(plan, workspace, workspace_bytes, -1, (hipStream_t)stream);
+}
+
+int paged_prefill_nvfp4_a4q(const nvfp4kv_cache_t* cache, const void* q,
+                            const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                            const int32_t* block_table, int32_t block_table_stride, int32_t batch,
+                            int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                            int32_t num_qo_heads, float sm_scale, int32_t causal, void* out,
+                            int32_t out_dtype, float* lse, int32_t q_format, int32_t num_splits,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (q_format != NVFP4KV_A4Q_MXFP8 && q_format != NVFP4KV_A4Q_MXFP4)
+    return fail(NVFP4KV_EINVAL, "q_format %d unknown", q_format);
   if (int e = check_cache(cache)) return e;
-  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_kv_len < 0)
-    return fail(NVFP4KV_EINVAL, "negative size");
-  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
-  if (!q || !cu_seqlens_q || !kv_lens || !block_table || !out)
-    return fail(NVFP4KV_EINVAL, "q, cu_seqlens_q, kv_lens, block_table or out is NULL");
-  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4KV_EINVAL, "q/out must be 16-byte aligned");
-  if (num_qo_heads < 1 || num_qo_heads % cache->num_kv_heads)
-    return fail(NVFP4KV_EINVAL, "num_qo_heads %d is not a multiple of num_kv_heads %d", num_qo_heads,
-                cache->num_kv_heads);
-  const int g = num_qo_heads / cache->num_kv_heads;
-  if (!group_ok(g)) return fail(NVFP4KV_EUNSUPPORTED, "query group size %d unsupported", g);
-  // output rows (token, head) are indexed in 32 bits, with room for the merge grid's rounding
-  if ((long)total_q * num_qo_heads > (1L << 30))
-    return fail(NVFP4KV_EINVAL, "total_q x num_qo_heads = %ld rows: too large for one launch",
-                (long)total_q * num_qo_heads);
-  if (block_table_stride < (max_kv_len + 15) / 16)
-    return fail(NVFP4KV_EINVAL, "block_table_stride %d too small for max_kv_len %d",
-                block_table_stride, max_kv_len);
-  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "sm_scale must be > 0");
-  if (out_dtype != NVFP4KV_OUT_BF16 && out_dtype != NVFP4KV_OUT_F32)
-    return fail(NVFP4KV_EINVAL, "out_dtype %d unknown", out_dtype);
-  if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
-
-  const int nw = prefill_waves(max_q_len, g);
-  const int rows = 32 * nw / g;
-  const int q_tiles = (max_q_len + rows - 1) / rows;
-  const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);
-  const long items = (long)cache->num_kv_heads * batch * q_tiles * s;
-  if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
-
-  nvfp4kv::PrefillParams p{};
-  p.format = cache->kv_format;
-  p.k_data = cache->k_data;
-  p.k_scale = cache->k_scale;
-  p.v_data = cache->v_data;
-  p.v_scale = cache->v_scale;
-  p.q = (const uint16_t*)q;
-  p.cu_q = cu_seqlens_q;
-  p.kv_lens = kv_lens;
-  p.block_table = block_table;
-  p.bt_stride = block_table_stride;
-  p.batch = batch;
-  p.num_kv_heads = cache->num_kv_heads;
-  p.num_qo_heads = num_qo_heads;
-  p.group = g;
-  p.q_tiles = q_tiles;
-  p.num_splits = s;
-  p.causal = causal ? 1 : 0;
-  p.total_q = total_q;
-  p.total_items = (int)items;
-  p.items_per_xcd = (int)((items + 7) / 8);
-  p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
-  p.out_scale = cache->v_global;
-  p.out_f32 = out_dtype == NVFP4KV_OUT_F32;
-  hipStream_t st = (hipStream_t)stream;
-  if (s > 1) {
-    const size_t need = (size_t)s * total_q * num_qo_heads * kPartRowBytes;
-    if (!workspace || workspace_bytes < need)
-      return fail(NVFP4KV_EWORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(NVFP4KV_EINVAL, "workspace must be 16-byte aligned");
-    p.part_o = (uint16_t*)workspace;
-    p.part_lse = (float*)(p.part_o + (size_t)s * total_q * num_qo_heads * 128);
-    p.lse = nullptr;
-    p.out = nullptr;
-    if (int e = check_launch(nvfp4kv::launch_prefill(p, nw, st), "prefill launch")) return e;
-    nvfp4kv::MergeParams m{};
-    m.part_o = p.part_o;
-    m.part_lse = p.part_lse;
-    m.num_splits = s;
-    m.rows = total_q * num_qo_heads;
-    m.out_scale = cache->v_global;
-    m.out = out;
-    m.out_f32 = p.out_f32;
-    m.lse = lse;
-    return check_launch(nvfp4kv::launch_merge(m, st), "merge launch");
-  }
-  p.lse = lse;
-  p.out = out;
-  return check_launch(nvfp4kv::launch_prefill(p, nw, st), "prefill launch");
+  if (cache->kv_format != NVFP4KV_FORMAT_NVFP4)
+    return fail(NVFP4KV_EUNSUPPORTED, "the A4Q-style prefill reads NVFP4 caches only");
+  PrefillPlan plan;
+  if (int e = plan_prefill(cache, q, cu_seqlens_q, kv_lens, block_table, block_table_stride, batch,
+                           total_q, max_q_len, max_kv_len, num_qo_heads, sm_scale, causal, out,
+                           out_dtype, lse, num_splits, true, &plan))
+    return e;
+  if (plan.empty) return ok();
+  return launch_prefill_plan(plan, workspace, workspace_bytes, q_format, (hipStream_t)stream);
 }
 
 size_t paged_decode_nvfp4_workspace_size(int32_t batch, int32_t max_kv_len, int32_t num_qo_heads,

@@ -126,6 +126,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 hipError_t launch_repack(const RepackParams& p, int batch, int max_pages, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream);
+// A4Q-style prefill (8-wave kernel; NVFP4 cache only); q_format 0 = MXFP8, 1 = MXFP4 queries.
+hipError_t launch_prefill_a4q(const PrefillParams& p, int q_format, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 

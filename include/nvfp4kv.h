@@ -179,6 +179,34 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
                         void* stream);
 
 /*
+ * A4Q-style prefill ([A] "Quantize Q instead of expanding K": the query is quantized inside the
+ * kernel and QK runs on a low-precision matrix product; "Make query accuracy a release gate": the
+ * added error is measured against the oracle).  Same arguments, semantics and workspace rules as
+ * paged_prefill_nvfp4 (its own *_workspace_size), plus:
+ *   q_format  NVFP4KV_A4Q_MXFP8: each query row's 128 values in blocks of 32 consecutive values,
+ *             scale 2^(floor(log2 amax) - 8) (E8M0), elements E4M3 nearest-even saturating at
+ *             448; NVFP4KV_A4Q_MXFP4: the same with E2M1 elements and 2^(floor(log2 amax) - 2),
+ *             saturating at 6.
+ * K is fed to gfx950's block-scaled MFMA as two E4M3 terms per value under one power-of-two scale
+ * per 32 values (exact when a key's two 16-value block scales in each 32-value block are within
+ * 2^8 of each other); softmax and PV are those of paged_prefill_nvfp4.  NVFP4 caches only
+ * (other formats: NVFP4KV_EUNSUPPORTED).  Every query-tile width runs the 8-wave kernel.
+ */
+#define NVFP4KV_A4Q_MXFP8 0
+#define NVFP4KV_A4Q_MXFP4 1
+size_t paged_prefill_nvfp4_a4q_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len,
+                                              int32_t max_kv_len, int32_t num_qo_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t num_splits);
+int paged_prefill_nvfp4_a4q(const nvfp4kv_cache_t* cache, const void* q,
+                            const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                            const int32_t* block_table, int32_t block_table_stride, int32_t batch,
+                            int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
+                            int32_t num_qo_heads, float sm_scale, int32_t causal, void* out,
+                            int32_t out_dtype, float* lse, int32_t q_format, int32_t num_splits,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Single-token paged decode ([B] "Decode can win on fewer bytes read": each step scans the whole
  * cache of a sequence for its one new query, after that token's K/V has been written).  Split-KV: each (sequence, KV head, split)
  * computes a partial softmax over its slice of the cache; a merge combines the partials.

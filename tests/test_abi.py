@@ -255,3 +255,30 @@ def test_noalloc_decode_rejects_more_than_its_scratch():
     assert dec(q=None) == -1
     assert dec(hq=8 * 32) == -2
     assert dec(batch=0) == 0 and _err() == ""
+
+
+def test_a4q_prefill_argument_checks():
+    """The A4Q-style prefill: unknown query formats and non-NVFP4 caches are refused, the other
+    checks are the stock prefill's, and its workspace follows the 8-wave kernel's split rule."""
+    lib = load_library()
+
+    def call(d, **kw):
+        a = dict(q=16, cu=16, kv=16, bt=16, bts=8, batch=1, total_q=16, max_q=16, max_kv=128,
+                 hq=32, sm=0.088, causal=1, out=16, odt=0, lse=None, qf=0, splits=0, ws=None, wsb=0)
+        a.update(kw)
+        return lib.paged_prefill_nvfp4_a4q(ctypes.byref(d), a["q"], a["cu"], a["kv"], a["bt"],
+                                           a["bts"], a["batch"], a["total_q"], a["max_q"],
+                                           a["max_kv"], a["hq"], a["sm"], a["causal"], a["out"],
+                                           a["odt"], a["lse"], a["qf"], a["splits"], a["ws"],
+                                           a["wsb"], None)
+    d = _desc()
+    assert call(d, qf=2) == -1 and "q_format" in _err()
+    assert call(_desc(kv_format=1, k_scale=None, v_scale=None)) == -2 and "NVFP4" in _err()
+    assert call(d, hq=30) == -1 and "multiple" in _err()
+    assert call(d, bts=2) == -1 and "block_table_stride" in _err()
+    assert call(d, total_q=0) == 0 and _err() == ""
+    need = A.prefill_a4q_workspace_size(1, 16, 16, 128, 32, 8, num_splits=4)
+    assert need == 4 * 16 * 32 * (128 * 2 + 4)
+    assert call(d, splits=4) == -3 and str(need) in _err()
+    # short tails run the 8-wave kernel (256 columns per tile), so the split count differs
+    assert A.prefill_a4q_workspace_size(8, 128, 16, 16384, 32, 8) > 0
