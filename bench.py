@@ -9,7 +9,8 @@ GB/s, and times the CPU oracle on a bounded sample of the prefill workload.  The
 cache (one E4M3FN byte per value) is timed on the 16K prefill, the decode loop and the short
 prefill shapes, with NVFP4 / FP8 time ratios; the dequantize-ahead repack (NVFP4 pages to an
 fp16 copy, then the prefill over the copy) is timed on the short shapes against the stock
-prefill.
+prefill.  The A4Q-style prefill (query quantized in the kernel, QK on the block-scaled MFMA) is
+timed against the stock prefill at 16K and on the 4 x 128 over 2K tails.
 
 Algorithmic work (nothing masked, padded or re-read is counted):
   prefill FLOP = 4 * head_dim * Hq * sum_b [q_b (kv_b - q_b) + q_b (q_b + 1) / 2]
@@ -386,6 +387,54 @@ def _blas_threads():
         return None
 
 
+def run_a4q(name, torch, A, reps=20):
+    """The A4Q-style prefill (query quantized to MX blocks in the kernel, QK on the block-scaled
+    MFMA; MXFP8 and MXFP4 queries) against the stock prefill on the same cache: median µs per
+    call, with a 512 MB buffer written before each call for the short shape (cold caches) and
+    back to back for the full one."""
+    pc = prefill_case(name)
+    w = pc.w
+    cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
+    A.append(cache, bf16_dev(pc.k_bits, torch), bf16_dev(pc.v_bits, torch),
+             torch.from_numpy(pc.slot_mapping).cuda())
+    q = bf16_dev(pc.q_bits, torch)
+    cu = torch.from_numpy(pc.cu_seqlens_q).cuda()
+    kv = torch.from_numpy(pc.kv_lens).cuda()
+    bt = torch.from_numpy(pc.layout.block_table).cuda()
+    out = torch.empty((pc.total_q, w.num_qo_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = max(A.prefill_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
+                                            w.num_qo_heads, w.num_kv_heads),
+                   A.prefill_a4q_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
+                                                w.num_qo_heads, w.num_kv_heads))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if w.batch > 1 else None
+    calls = {
+        "stock": lambda: A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale,
+                                   out=out, workspace=ws),
+        "a4q_mxfp8": lambda: A.prefill_a4q(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len,
+                                           w.sm_scale, q_format="mxfp8", out=out, workspace=ws),
+        "a4q_mxfp4": lambda: A.prefill_a4q(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len,
+                                           w.sm_scale, q_format="mxfp4", out=out, workspace=ws),
+    }
+    res = {"workload": name, "mode": "flushed" if flush is not None else "warm"}
+    for key, fn in calls.items():
+        warm_up(fn, torch)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in ev:
+            if flush is not None:
+                flush.zero_()
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        res["us_" + key] = round(float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3, 2)
+    for key in ("a4q_mxfp8", "a4q_mxfp4"):
+        res["ratio_" + key + "_over_stock"] = round(res["us_" + key] / res["us_stock"], 3)
+    flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
+    res["TFLOPs_a4q_mxfp8"] = round(flops / (res["us_a4q_mxfp8"] * 1e-6) / 1e12, 2)
+    return res
+
+
 def run_cpu_baseline(pc, target_s=CPU_TARGET_S):
     """The oracle, untuned, on a bounded sample of the 16K prefill: all 32 heads of query rows
     spread evenly over the sequence (their visible keys included), after the oracle's append of
@@ -532,6 +581,7 @@ def main():
                     help="skip the tiny / tail128 / tail16 prefill timings (stock; repacked for the tails)")
     ap.add_argument("--no-matrix", action="store_true", help="skip the full 8K / 32K prefill timings")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 control-cache timings")
+    ap.add_argument("--no-a4q", action="store_true", help="skip the A4Q-style prefill timings")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -580,6 +630,8 @@ def main():
                                     for n in ("tiny", "tail128", "tail16")]
     if not args.no_short:
         line["repack"] = [run_repack_prefill(n, torch, A) for n in ("tail128", "tail16")]
+    if not args.no_a4q:
+        line["a4q"] = [run_a4q(n, torch, A) for n in ("full16k", "tail128")]
     if not args.no_matrix:
         line["prefill_matrix"] = [run_full_prefill(n, torch, A) for n in ("full8k", "full32k")]
         if not args.no_fp8:

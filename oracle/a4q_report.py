@@ -14,6 +14,11 @@ float64 attention with the bf16 queries as given.  Cases:
 * tail16 (8 x 16 queries over 16,384 keys), sequences 0 and 5;
 * full16k and full32k, 24 evenly spaced query rows.
 
+Schemes: the pages' reading (``a4q.SCHEMES`` through ``prefill_a4q``: QK exact on the quantized
+query, weights rounded to bf16 for PV) and the scheme of the GPU variant
+(``prefill_mx`` with "mxfp8" / "mxfp4" queries: K through its two-term E4M3 bridge, float64
+softmax and PV), listed as ``gpu:mxfp8`` and ``gpu:mxfp4``.
+
 Run: ``python -m oracle.a4q_report`` (prints a markdown table).
 """
 from __future__ import annotations
@@ -29,7 +34,7 @@ def _cache_of(pc, seqs=None):
     oc = cache.PagedCache(pc.layout.num_pages, pc.w.num_kv_heads)
     for b in (range(pc.w.batch) if seqs is None else seqs):
         s0, s1 = pc.cu_seqlens_kv[b], pc.cu_seqlens_kv[b + 1]
-        oc.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1])
+        oc.append(pc.k_bits[s0:s1], pc.v_bits[s0:s1], pc.slot_mapping[s0:s1], workers=8)
     return oc
 
 
@@ -59,9 +64,14 @@ def main():
         ref, _ = attention.prefill(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
                                    pc.w.sm_scale, causal=causal, rows=rows)
         m = ~np.isnan(ref)
-        for scheme in a4q.SCHEMES:
-            o = a4q.prefill_a4q(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
-                                pc.w.sm_scale, scheme, causal=causal, rows=rows)
+        for scheme in a4q.SCHEMES + ("gpu:mxfp8", "gpu:mxfp4"):
+            if scheme.startswith("gpu:"):
+                o = a4q.prefill_mx(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
+                                   pc.w.sm_scale, scheme[4:], causal=causal, rows=rows)
+            else:
+                o = a4q.prefill_a4q(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens,
+                                    pc.layout.block_table, pc.w.sm_scale, scheme, causal=causal,
+                                    rows=rows)
             err = np.abs(o[m] - ref[m])
             ok = "yes" if err.max() <= 1e-2 and err.mean() <= 1e-3 else "no"
             print(f"| {name} | {scheme} | {err.max():.3e} | {err.mean():.3e} | {ok} |", flush=True)
