@@ -106,17 +106,18 @@ int prefill_splits(int batch, int q_tiles, int num_kv_heads, int max_kv_len, int
 // workgroups (two thirds of the 768 the GPU holds at once): measured on 1, 4, 16 and 64 sequences
 // of 16K-32K keys, more slices only add workgroup set-up and merge work.  Long caches are sliced
 // further by the per-slice key limit below.
-int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, int* chunk) {
+int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, int* chunk,
+                  long target = 512, int chunk_max = kDecodeChunkMax) {
   int s = requested;
   if (s <= 0) {
     const long pairs = (long)batch * num_kv_heads;
-    const long want = std::max(1L, (512 + pairs - 1) / pairs);
+    const long want = std::max(1L, (target + pairs - 1) / pairs);
     const long cap = std::max(1, (max_kv_len + kDecodeChunkMin - 1) / kDecodeChunkMin);
     s = (int)std::min(want, cap);
   }
   // slice length: a multiple of 4 waves x 32 tokens covering max_kv_len in s slices, and at
   // most 4 x 2048 keys (each wavefront keeps its slice's page ids in two registers)
-  s = std::max(s, (max_kv_len + kDecodeChunkMax - 1) / kDecodeChunkMax);
+  s = std::max(s, (max_kv_len + chunk_max - 1) / chunk_max);
   int c = (max_kv_len + s - 1) / s;
   c = ((c + 127) / 128) * 128;
   if (c < 128) c = 128;
@@ -126,16 +127,36 @@ int decode_splits(int batch, int num_kv_heads, int max_kv_len, int requested, in
 
 bool group_ok(int g) { return g >= 1 && g <= 64 && (256 % g) == 0; }
 
-// Prefill arguments checked and turned into kernel parameters (a8 = the A4Q-style kernel, which
-// always runs the 8-wave kernel); the workspace pointers are filled by launch_prefill_plan.
+// Prefill arguments checked and turned into kernel parameters (a4q = the A4Q-style kernel, which
+// always runs the 8-wave kernel; otherwise up to 64 query columns per (sequence, KV head) take
+// the short-query kernel on NVFP4 and FP8 caches); the workspace pointers are filled by
+// launch_prefill_plan.
 struct PrefillPlan {
   nvfp4kv::PrefillParams p;
   int nw;
+  int ncb;  // > 0: the short-query kernel with this many column blocks
   bool empty;
   size_t workspace_bytes;
   void* out;
   float* lse;
 };
+
+// Short-query kernel for `cols` query columns per (sequence, KV head): 1 or 2 = four wavefronts
+// on key quarters with that many 16-column blocks each, 4 = four wavefronts of 16 columns sharing
+// one conversion of each key; 0 above 64 columns, where the tile kernels take over.
+int tail_blocks(long cols) {
+  if (cols > 64) return 0;
+  return cols > 32 ? 4 : cols > 16 ? 2 : 1;
+}
+
+// Key slices per (sequence, KV head) of the short-query kernel, chosen like the decode's: about
+// 1024 workgroups of at most 2048 keys for the 64-column kernel (four workgroups per CU), 512
+// workgroups of at most 8192 keys (4 quarters x 2048) for the others; at least 512 keys per slice.
+int tail_splits(int batch, int ncb, int num_kv_heads, int max_kv_len, int requested, int* chunk) {
+  const int kv = std::max(max_kv_len, 1);
+  if (ncb == 4) return decode_splits(batch, num_kv_heads, kv, requested, chunk, 1024, 2048);
+  return decode_splits(batch, num_kv_heads, kv, requested, chunk, 512, 8192);
+}
 
 size_t prefill_workspace(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_kv_len,
                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -148,8 +169,15 @@ size_t prefill_workspace(int32_t batch, int32_t total_q, int32_t max_q_len, int3
   const int nw = a4q ? 8 : prefill_waves(max_q_len, g);
   const int q_tiles = (max_q_len + (32 * nw / g) - 1) / (32 * nw / g);
   const int s = prefill_splits(batch, q_tiles, num_kv_heads, max_kv_len, nw, num_splits);
-  if (s <= 1) return 0;
-  return (size_t)s * total_q * num_qo_heads * kPartRowBytes;
+  size_t bytes = s > 1 ? (size_t)s * total_q * num_qo_heads * kPartRowBytes : 0;
+  // up to 64 columns the NVFP4 and FP8 caches take the short-query kernel, which always writes
+  // slice partials; the fp16 (repacked) cache keeps the tile kernel: size for either
+  if (const int ncb = a4q ? 0 : tail_blocks((long)max_q_len * g)) {
+    int chunk = 0;
+    const int st = tail_splits(batch, ncb, num_kv_heads, max_kv_len, num_splits, &chunk);
+    bytes = std::max(bytes, (size_t)st * total_q * num_qo_heads * kPartRowBytes);
+  }
+  return bytes;
 }
 
 int plan_prefill(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_seqlens_q,
@@ -186,9 +214,12 @@ int plan_prefill(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_
   if (num_splits < 0) return fail(NVFP4KV_EINVAL, "num_splits < 0");
 
   const int nw = a4q ? 8 : prefill_waves(max_q_len, g);
+  const int ncb = (a4q || cache->kv_format == NVFP4KV_FORMAT_F16) ? 0 : tail_blocks((long)max_q_len * g);
   const int rows = 32 * nw / g;
-  const int q_tiles = (max_q_len + rows - 1) / rows;
-  const int s = prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);
+  const int q_tiles = ncb ? 1 : (max_q_len + rows - 1) / rows;
+  int chunk = 0;
+  const int s = ncb ? tail_splits(batch, ncb, cache->num_kv_heads, max_kv_len, num_splits, &chunk)
+                    : prefill_splits(batch, q_tiles, cache->num_kv_heads, max_kv_len, nw, num_splits);
   const long items = (long)cache->num_kv_heads * batch * q_tiles * s;
   if (items > (1L << 30)) return fail(NVFP4KV_EINVAL, "problem too large for one launch");
 
@@ -217,10 +248,12 @@ int plan_prefill(const nvfp4kv_cache_t* cache, const void* q, const int32_t* cu_
   p.score_scale = sm_scale * cache->k_global * 1.4426950408889634f;
   p.out_scale = cache->v_global;
   p.out_f32 = out_dtype == NVFP4KV_OUT_F32;
+  p.chunk = chunk;
   plan->nw = nw;
+  plan->ncb = ncb;
   plan->out = out;
   plan->lse = lse;
-  plan->workspace_bytes = s > 1 ? (size_t)s * total_q * num_qo_heads * kPartRowBytes : 0;
+  plan->workspace_bytes = (s > 1 || ncb) ? (size_t)s * total_q * num_qo_heads * kPartRowBytes : 0;
   return NVFP4KV_OK;
 }
 
@@ -230,10 +263,10 @@ int launch_prefill_plan(PrefillPlan& plan, void* workspace, size_t workspace_byt
                         hipStream_t st) {
   nvfp4kv::PrefillParams& p = plan.p;
   auto launch = [&]() {
-    return q_format < 0 ? nvfp4kv::launch_prefill(p, plan.nw, st)
-                        : nvfp4kv::launch_prefill_a4q(p, q_format, st);
+    if (q_format >= 0) return nvfp4kv::launch_prefill_a4q(p, q_format, st);
+    return plan.ncb ? nvfp4kv::launch_prefill_tail(p, plan.ncb, st) : nvfp4kv::launch_prefill(p, plan.nw, st);
   };
-  if (p.num_splits > 1) {
+  if (p.num_splits > 1 || plan.ncb) {
     if (!workspace || workspace_bytes < plan.workspace_bytes)
       return fail(NVFP4KV_EWORKSPACE, "prefill needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                   workspace ? workspace_bytes : (size_t)0);

@@ -68,6 +68,7 @@ struct PrefillParams {
   uint16_t* part_o;       // split mode: fp16 [num_splits][total_q][Hq][D]
   float* part_lse;        // split mode: [num_splits][total_q][Hq] (log2 units)
   int32_t format;         // cache format: 0 NVFP4, 1 FP8 E4M3FN, 2 fp16 (repacked)
+  int32_t chunk;          // short-query kernel: keys per split (multiple of 128)
 };
 
 struct RepackParams {
@@ -129,6 +130,11 @@ hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream)
 // A4Q-style prefill (8-wave kernel; NVFP4 cache only); q_format 0 = MXFP8, 1 = MXFP4 queries.
 hipError_t launch_prefill_a4q(const PrefillParams& p, int q_format, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+// Short-query prefill (up to 64 query columns per sequence and KV head; p.chunk keys per slice,
+// at most 8192, or 2048 for ncb 4): ncb 1 or 2 column blocks of 16 per wavefront on key
+// quarters, 4 = four wavefronts of 16 columns sharing each key's conversion; always writes split
+// partials (p.part_o / p.part_lse) for launch_merge.
+hipError_t launch_prefill_tail(const PrefillParams& p, int ncb, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace nvfp4kv

@@ -144,11 +144,12 @@ def test_prefill_group_sizes(hq, hkv):
 
 
 @pytest.mark.parametrize("kv_format", ["nvfp4", "fp8"])
-@pytest.mark.parametrize("q_max", [8, 9, 16, 17, 32, 33, 64, 65])
+@pytest.mark.parametrize("q_max", [4, 5, 8, 9, 16, 17, 32, 33, 64, 65])
 def test_prefill_kernel_boundaries(q_max, kv_format):
-    """Query tiles on each side of the kernel choices at group size 4 (32 / 8 heads): up to 64
-    columns (16 rows) the key-split kernel, 65-128 the four-wave kernel, above 128 the 8-wave
-    kernel; the longest sequence decides, the shorter one rides in padded tiles."""
+    """Query tiles on each side of the kernel choices at group size 4 (32 / 8 heads): up to 16
+    columns (4 rows) the short-query kernel with one 16-column block, up to 32 with two, up to 64
+    (16 rows) its four-wavefront shared-conversion form, 65-128 the four-wave tile kernel, above
+    128 the 8-wave kernel; the longest sequence decides, the shorter one rides along."""
     say(f"[prefill] kernel boundary: max q_len {q_max} ({4 * q_max} columns), {kv_format}")
     pc = _case([q_max, max(1, q_max // 3)], [q_max + 700, q_max // 3 + 90], seed=3020 + q_max, k_out=10)
     g = GpuPrefillCase(pc, kv_format=kv_format)
