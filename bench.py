@@ -45,7 +45,7 @@ PEAK_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_full16k_prefill_decode_b64.json")
 PREFILL_KERNEL = "nvfp4_prefill_staggered_kernel<0>"  # the NVFP4 instantiation
-PREFILL_SOURCES = ["prefill.hip", "device_common.hpp", "kernel_params.hpp"]
+PREFILL_SOURCES = ["prefill.hip", "prefill_common.hpp", "device_common.hpp", "kernel_params.hpp"]
 DECODE_KERNEL = "nvfp4_decode_kernel<0>"
 DECODE_SOURCES = ["decode.hip", "device_common.hpp", "kernel_params.hpp"]
 CPU_TARGET_S = 12.0  # seconds of oracle work the timed CPU sample aims at
@@ -222,10 +222,18 @@ def decode_result(w, fmt, lens_np, ev, loop_s):
     return out
 
 
+def make_flush(torch):
+    """A 512 MB read between timed calls: it refills the L2s and the 256 MB MALL with clean lines
+    of another buffer, so the timed call reads its cache from HBM.  (Writing such a buffer
+    instead would leave up to a MALL of dirty lines that the timed call has to write back.)"""
+    buf = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    return lambda: buf.max()
+
+
 def run_repack_prefill(name, torch, A, reps=20):
     """Dequantize-ahead repack on a short-query workload: median µs of the repack pass (every
     page the batch reads, NVFP4 -> fp16 copy), of the prefill over the copy, and of both
-    together, with a 512 MB buffer written before each call (cold caches), against the stock
+    together, with a 512 MB buffer read before each call (cold caches), against the stock
     prefill over the packed cache measured the same way."""
     pc = prefill_case(name)
     w = pc.w
@@ -241,7 +249,7 @@ def run_repack_prefill(name, torch, A, reps=20):
     ws_bytes = A.prefill_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
                                         w.num_qo_heads, w.num_kv_heads)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = make_flush(torch)
 
     def prefill(c):
         A.prefill(c, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out, workspace=ws)
@@ -254,13 +262,13 @@ def run_repack_prefill(name, torch, A, reps=20):
     warm_up(both, torch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
     for i in range(reps):
-        flush.zero_()
+        flush()
         ev[i][0].record()
         A.repack(cache, dst, bt, kv, pc.max_kv_len)
         ev[i][1].record()
         prefill(dst)
         ev[i][2].record()
-        flush.zero_()
+        flush()
         ev[i][3].record()
         prefill(cache)
         ev[i][4].record()
@@ -334,7 +342,7 @@ def run_full_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
 def run_short_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
     """Prefill-only timing of a short workload (tiny: 1 x 256 queries over 256 keys, 4 / 1 heads;
     tail128: 4 x 128 queries over 2,048 keys; tail16: 8 x 16 queries over 16,384 keys): median µs
-    per call with a 512 MB buffer written
+    per call with a 512 MB buffer read
     between calls (flushing L2 and MALL, so the packed cache comes from HBM) and warm
     back-to-back, with algorithmic TFLOP/s and GB/s (Q + O + packed KV of every sequence)."""
     pc = prefill_case(name)
@@ -350,7 +358,7 @@ def run_short_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
     ws_bytes = A.prefill_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
                                         w.num_qo_heads, w.num_kv_heads)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = make_flush(torch)
 
     def call():
         A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale, out=out,
@@ -362,7 +370,7 @@ def run_short_prefill(name, torch, A, reps=20, kv_format="nvfp4"):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for i in range(reps):
             if mode == "flushed":
-                flush.zero_()
+                flush()
             ev[i][0].record()
             call()
             ev[i][1].record()
@@ -390,7 +398,7 @@ def _blas_threads():
 def run_a4q(name, torch, A, reps=20):
     """The A4Q-style prefill (query quantized to MX blocks in the kernel, QK on the block-scaled
     MFMA; MXFP8 and MXFP4 queries) against the stock prefill on the same cache: median µs per
-    call, with a 512 MB buffer written before each call for the short shape (cold caches) and
+    call, with a 512 MB buffer read before each call for the short shape (cold caches) and
     back to back for the full one."""
     pc = prefill_case(name)
     w = pc.w
@@ -407,7 +415,7 @@ def run_a4q(name, torch, A, reps=20):
                    A.prefill_a4q_workspace_size(w.batch, pc.total_q, pc.max_q_len, pc.max_kv_len,
                                                 w.num_qo_heads, w.num_kv_heads))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if w.batch > 1 else None
+    flush = make_flush(torch) if w.batch > 1 else None
     calls = {
         "stock": lambda: A.prefill(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len, w.sm_scale,
                                    out=out, workspace=ws),
@@ -422,7 +430,7 @@ def run_a4q(name, torch, A, reps=20):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for e in ev:
             if flush is not None:
-                flush.zero_()
+                flush()
             e[0].record()
             fn()
             e[1].record()
@@ -560,14 +568,22 @@ def fp8_summary(line, fp8):
     return out
 
 
-def copy_calibration(torch, nbytes=1 << 30):
-    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}))
+def copy_calibration(torch, sizes=(1 << 30, 1 << 26)):
+    """Plain device copies of known sizes, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE: 1 GiB,
+    and 64 MiB, about the bf16 K and V that the 16K append reads (each copy's grid size tells the
+    launches apart)."""
+    for nbytes in sizes:
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}))
+
+
+def progress(msg):
+    """One line per leg on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {time.strftime('%H:%M:%S')} {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -596,6 +612,7 @@ def main():
         copy_calibration(torch)
         return
 
+    progress("full16k append + prefill")
     pre = run_prefill(args, torch, A)
     value = pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12
     achieved = pre["flops"] / (pre["prefill_ms"] * 1e-3) / 1e12
@@ -618,28 +635,35 @@ def main():
                    "GBps": round(pre["append_bytes"] / (pre["append_ms"] * 1e-3) / 1e9, 1)},
     }
     fp8 = {}
+    progress("decode loop")
     if not args.no_decode:
         dec = run_decode(args, torch, A, ("nvfp4",) if args.no_fp8 else ("nvfp4", "fp8"))
         line["decode"] = dec["nvfp4"]
         if "fp8" in dec:
             fp8["decode"] = dec["fp8"]
+    progress("short prefill legs")
     if not args.no_short:
         line["short_prefill"] = [run_short_prefill(n, torch, A) for n in ("tiny", "tail128", "tail16")]
         if not args.no_fp8:
             fp8["short_prefill"] = [run_short_prefill(n, torch, A, kv_format="fp8")
                                     for n in ("tiny", "tail128", "tail16")]
+    progress("repack legs")
     if not args.no_short:
         line["repack"] = [run_repack_prefill(n, torch, A) for n in ("tail128", "tail16")]
+    progress("A4Q legs")
     if not args.no_a4q:
         line["a4q"] = [run_a4q(n, torch, A) for n in ("full16k", "tail128")]
+    progress("8K / 32K prefill legs")
     if not args.no_matrix:
         line["prefill_matrix"] = [run_full_prefill(n, torch, A) for n in ("full8k", "full32k")]
         if not args.no_fp8:
             fp8["prefill_matrix"] = [run_full_prefill(n, torch, A, kv_format="fp8")
                                      for n in ("full8k", "full32k")]
+    progress("FP8 16K prefill leg")
     if not args.no_fp8:
         fp8["prefill_full16k"] = run_full_prefill("full16k", torch, A, kv_format="fp8")
         line["fp8_control"] = fp8_summary(line, fp8)
+    progress("CPU oracle baseline")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(pre["pc"])
         line["cpu_baseline"]["phases"] = run_cpu_phases()
