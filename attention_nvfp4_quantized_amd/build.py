@@ -14,7 +14,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.cpp", "append.hip", "dequant.hip", "prefill.hip", "prefill_a4q.hip", "tail.hip", "decode.hip"]
+SOURCES = ["api.cpp", "append.hip", "dequant.hip", "prefill.hip", "prefill_a4q.hip", "tail.hip", "decode.hip",
+           "merge.hip"]
 LIB_NAME = "libnvfp4kv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"

@@ -161,9 +161,11 @@ __device__ __forceinline__ void decode_step(const DecodeRegs<FMT>& r, int k, int
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(sc[0][j], sc[1][j]));
-  mx = pair32_max(pair16_max(mx)) * cs;
+  // the column maximum (across the four lanes holding the column) is only needed when some
+  // lane's own maximum exceeds the reference by more than 8
+  mx *= cs;
   if (wave_any(mx > st.m_used + 8.0f)) {
-    const float m_new = fmaxf(st.m_used, mx);
+    const float m_new = fmaxf(st.m_used, pair32_max(pair16_max(mx)));
     const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(st.m_used - m_new);
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;

@@ -384,50 +384,6 @@ __global__ __launch_bounds__(64 * kStagWaves) void nvfp4_prefill_staggered_kerne
   prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
 
-// Log-sum-exp merge of split partials (fp16 values, float32 log-sum-exps): one wavefront per
-// (query row, head); lane l owns head-dim values 2l and 2l+1.  The lanes read the slices' log-sum-exps in parallel and take
-// their maximum across the wavefront; the partials are then read eight slices at a time with
-// the eight loads issued together (a partial of an empty slice is read but not used: it is not
-// written), and accumulated in slice order.
-__global__ __launch_bounds__(256) void nvfp4_merge_kernel(MergeParams p) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.rows) return;
-  const int lane = threadIdx.x & 63;
-  const int S = p.num_splits;
-  float mx = kNegInf;
-  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, p.part_lse[(int64_t)s * p.rows + row]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-  float wsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  if (mx != kNegInf) {
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      float ls[8];
-      f16x2 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t r = (int64_t)min(s0 + j, S - 1) * p.rows + row;
-        ls[j] = p.part_lse[r];
-        v[j] = *(const f16x2*)(p.part_o + r * kHeadDim + 2 * lane);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool use = s0 + j < S && ls[j] != kNegInf;
-        const float wgt = use ? fast_exp2(ls[j] - mx) : 0.0f;
-        wsum += wgt;
-        o0 = use ? fmaf(wgt, (float)v[j][0], o0) : o0;
-        o1 = use ? fmaf(wgt, (float)v[j][1], o1) : o1;
-      }
-    }
-  }
-  const float inv = wsum > 0.0f ? p.out_scale / wsum : 0.0f;
-  if (p.out_f32) {
-    *(f32x2*)((float*)p.out + (int64_t)row * kHeadDim + 2 * lane) = f32x2{o0 * inv, o1 * inv};
-  } else {
-    *(uint32_t*)((uint16_t*)p.out + (int64_t)row * kHeadDim + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
-  }
-  if (p.lse && lane == 0) p.lse[row] = wsum > 0.0f ? (mx + __log2f(wsum)) * kLn2 : kNegInf;
-}
-
 template <int FMT>
 hipError_t launch_prefill_fmt(const PrefillParams& p, int waves, hipStream_t stream) {
   const dim3 grid((unsigned)(8 * p.items_per_xcd));
@@ -449,12 +405,6 @@ hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream)
     case kFmtF16: return launch_prefill_fmt<kFmtF16>(p, waves, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.rows + 3) / 4));
-  hipLaunchKernelGGL(nvfp4_merge_kernel, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
 }
 
 }  // namespace nvfp4kv
