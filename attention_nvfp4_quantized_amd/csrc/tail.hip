@@ -56,7 +56,8 @@ __device__ __forceinline__ int tail_page(int pt0, int pt1, int pi) {
 
 // Loads of one plane for the 32 keys starting at k, unconditional: a group past the quarter's
 // range re-reads its last group (an empty range reads its first page), and keys past the range
-// are zeroed at use.
+// are zeroed at use.  Each cache byte is read by one workgroup once, so the loads are
+// non-temporal (streaming).
 template <int FMT>
 __device__ __forceinline__ void plane_load(const PrefillParams& p, const uint8_t* data,
                                            const uint8_t* scale, int hk, int wk0, int wk1, int pt0,
@@ -69,12 +70,12 @@ __device__ __forceinline__ void plane_load(const PrefillParams& p, const uint8_t
     const int page = tail_page(pt0, pt1, (first - wk0) >> 4);
     const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (lane & 15);
     if constexpr (FMT == kFmtNvfp4) {
-      r.d[g] = *(const u32x4*)(data + row * kRowBytes + 16 * q4);
-      r.s[g] = *(const uint32_t*)(scale + row * kScaleBytes + 4 * (q4 >> 1));
+      r.d[g] = __builtin_nontemporal_load((const u32x4*)(data + row * kRowBytes + 16 * q4));
+      r.s[g] = __builtin_nontemporal_load((const uint32_t*)(scale + row * kScaleBytes + 4 * (q4 >> 1)));
     } else {
       const uint8_t* dp = data + row * kHeadDim + 32 * q4;
-      r.d[g] = *(const u32x4*)dp;
-      r.d2[g] = *(const u32x4*)(dp + 16);
+      r.d[g] = __builtin_nontemporal_load((const u32x4*)dp);
+      r.d2[g] = __builtin_nontemporal_load((const u32x4*)(dp + 16));
     }
   }
 }
@@ -455,12 +456,12 @@ __device__ __forceinline__ void group_load(const PrefillParams& p, const uint8_t
   const int page = tail_page(pt0, pt1, (first - wk0) >> 4);
   const int64_t row = ((int64_t)page * p.num_kv_heads + hk) * kPageSize + (lane & 15);
   if constexpr (FMT == kFmtNvfp4) {
-    r.d = *(const u32x4*)(data + row * kRowBytes + 16 * q4);
-    r.s = *(const uint32_t*)(scale + row * kScaleBytes + 4 * (q4 >> 1));
+    r.d = __builtin_nontemporal_load((const u32x4*)(data + row * kRowBytes + 16 * q4));
+    r.s = __builtin_nontemporal_load((const uint32_t*)(scale + row * kScaleBytes + 4 * (q4 >> 1)));
   } else {
     const uint8_t* dp = data + row * kHeadDim + 32 * q4;
-    r.d = *(const u32x4*)dp;
-    r.d2[0] = *(const u32x4*)(dp + 16);
+    r.d = __builtin_nontemporal_load((const u32x4*)dp);
+    r.d2[0] = __builtin_nontemporal_load((const u32x4*)(dp + 16));
   }
 }
 
