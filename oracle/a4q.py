@@ -166,6 +166,14 @@ def prefill_a4q(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, bl
 # values y = x / X (|y| < 384) are carried as two E4M3 terms, hi = E4M3_RNE(y) and
 # lo = E4M3_RNE(y - hi); the product sees X (hi + lo).  That equals x whenever lo is exact in
 # E4M3, which holds when the block's two scales lie within a factor 2^8 of each other.
+#
+# The one-term form keeps hi alone: the product sees X hi, one FP8 operand instead of two (half
+# the matrix-core work of QK).  It rounds K to E4M3's 4 significant bits under the block's
+# power-of-two scale: |X hi - x| <= 2^-4 |x| where |y| >= 2^-6 (E4M3's normal range), and at most
+# half the subnormal step, 2^-10 X, below it.  It is an approximation beyond the pages' A4Q, whose
+# product takes the cache's K exactly; where both 16-value block scales of a 32-value block are
+# powers of two within 2^13 of each other every y has at most 2 significant bits inside E4M3's
+# range and the one-term value is exact.
 
 def k_bridge(x: np.ndarray, s: np.ndarray):
     """Two-term E4M3 form of cache values x [..., D] (float64, exact s * e2m1 values) whose
@@ -186,21 +194,34 @@ def k_bridge(x: np.ndarray, s: np.ndarray):
     return hi, lo, e, bridged
 
 
-def gather_bridged_k(cache: PagedCache, block_table_row, n: int) -> np.ndarray:
-    """Bridged K values of positions 0..n-1 of one sequence: float64 [n][H][D]."""
+def k_one_term(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """One-term E4M3 form of cache values x [..., D] with 16-value block scales s [..., D/16]:
+    X e4m3(hi), with X and hi as in ``k_bridge`` (float64)."""
+    hi, _, e, _ = k_bridge(x, s)
+    return np.repeat(np.ldexp(1.0, e), MX_BLOCK, axis=-1) * codec.e4m3_value(hi)
+
+
+def gather_bridged_k(cache: PagedCache, block_table_row, n: int, k_terms: int = 2) -> np.ndarray:
+    """K values of positions 0..n-1 of one sequence as the block-scaled product sees them:
+    the two-term bridge (k_terms 2) or the one-term form (k_terms 1); float64 [n][H][D]."""
+    if k_terms not in (1, 2):
+        raise ValueError(f"k_terms must be 1 or 2, got {k_terms!r}")
     pos = np.arange(n)
     pages = np.asarray(block_table_row, dtype=np.int64)[pos // cache.page_size]
     kd, ks, _, _ = cache.token_rows(pages, pos % cache.page_size)
     x = codec.dequantize(kd, ks)
-    return k_bridge(x, codec.e4m3_value(ks))[3] * cache.k_global
+    s = codec.e4m3_value(ks)
+    kv = k_bridge(x, s)[3] if k_terms == 2 else k_one_term(x, s)
+    return kv * cache.k_global
 
 
 def prefill_mx(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, block_table,
-               sm_scale: float, q_format: str, causal: bool = True, rows=None):
+               sm_scale: float, q_format: str, causal: bool = True, rows=None, k_terms: int = 2):
     """The A4Q-style prefill that gfx950's block-scaled MFMA computes: each query row quantized
     by ``q_format`` ("mxfp8" or "mxfp4", blocks of 32 consecutive head-dim values), K as its
-    two-term E4M3 bridge, QK exact on those values, and then the oracle's plain float64
-    attention (softmax and PV on the cache's V, unrounded).  Arguments as ``prefill_a4q``."""
+    two-term E4M3 bridge (``k_terms`` 2) or its one-term form (1), QK exact on those values, and
+    then the oracle's plain float64 attention (softmax and PV on the cache's V, unrounded).
+    Other arguments as ``prefill_a4q``."""
     if q_format not in ("mxfp8", "mxfp4"):
         raise ValueError(f"q_format must be mxfp8 or mxfp4, got {q_format!r}")
     q = codec.bf16_to_f32(q_bits).astype(np.float64)
@@ -214,7 +235,7 @@ def prefill_mx(cache: PagedCache, q_bits: np.ndarray, cu_seqlens_q, kv_lens, blo
         idx = np.nonzero(want[q0:q1])[0]
         if len(idx) == 0:
             continue
-        kh = gather_bridged_k(cache, block_table[b], kvl)
+        kh = gather_bridged_k(cache, block_table[b], kvl, k_terms)
         _, vh = cache.gather(block_table[b], kvl)
         last = (kvl - (q1 - q0) + idx) if causal else np.full(len(idx), kvl - 1)
         qq = quantize_q(q[q0 + idx], q_format)

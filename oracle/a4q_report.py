@@ -17,7 +17,9 @@ float64 attention with the bf16 queries as given.  Cases:
 Schemes: the pages' reading (``a4q.SCHEMES`` through ``prefill_a4q``: QK exact on the quantized
 query, weights rounded to bf16 for PV) and the scheme of the GPU variant
 (``prefill_mx`` with "mxfp8" / "mxfp4" queries: K through its two-term E4M3 bridge, float64
-softmax and PV), listed as ``gpu:mxfp8`` and ``gpu:mxfp4``.
+softmax and PV), listed as ``gpu:mxfp8`` and ``gpu:mxfp4``, and its one-term K form
+(``k_terms=1``: K rounded to one E4M3 term under the block's power-of-two scale), listed as
+``gpu:mxfp8:k1`` and ``gpu:mxfp4:k1``.
 
 Run: ``python -m oracle.a4q_report`` (prints a markdown table).
 """
@@ -64,10 +66,12 @@ def main():
         ref, _ = attention.prefill(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
                                    pc.w.sm_scale, causal=causal, rows=rows)
         m = ~np.isnan(ref)
-        for scheme in a4q.SCHEMES + ("gpu:mxfp8", "gpu:mxfp4"):
+        for scheme in a4q.SCHEMES + ("gpu:mxfp8", "gpu:mxfp4", "gpu:mxfp8:k1", "gpu:mxfp4:k1"):
             if scheme.startswith("gpu:"):
+                fmt = scheme.split(":")[1]
                 o = a4q.prefill_mx(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens, pc.layout.block_table,
-                                   pc.w.sm_scale, scheme[4:], causal=causal, rows=rows)
+                                   pc.w.sm_scale, fmt, causal=causal, rows=rows,
+                                   k_terms=1 if scheme.endswith(":k1") else 2)
             else:
                 o = a4q.prefill_a4q(oc, q_bits, pc.cu_seqlens_q, pc.kv_lens,
                                     pc.layout.block_table, pc.w.sm_scale, scheme, causal=causal,

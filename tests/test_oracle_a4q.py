@@ -304,9 +304,10 @@ def test_pins_catch_mxfp8_without_saturation_bound():
             assert list(bad(x[i])) == _mx8_block_brute(x[i])
 
 
-def _bridge_brute(x_block, s_pair):
+def _bridge_brute(x_block, s_pair, terms=2):
     """The two-term bridge of one 32-value block by exact rationals: E from the larger scale,
-    X = 2^(E - 5); hi, lo nearest-even E4M3 (searched exhaustively) of y and y - hi."""
+    X = 2^(E - 5); hi, lo nearest-even E4M3 (searched exhaustively) of y and y - hi.  With
+    terms=1 the value is X hi alone."""
     def fl(sv):
         if sv == 0:
             return -15
@@ -330,7 +331,7 @@ def _bridge_brute(x_block, s_pair):
     for v in x_block:
         y = Fraction(float(v)) / X
         hi = near(y)
-        lo = near(y - hi)
+        lo = near(y - hi) if terms == 2 else 0
         out.append(float(X * (hi + lo)))
     return out
 
@@ -379,10 +380,74 @@ def test_pins_catch_k_bridge_without_the_low_term():
         assert np.array_equal(bad(xv, s)[3], xv)
 
 
-def check_prefill_mx_paged(prefill_mx, q_format, seed=27):
+# ---- the one-term form of K (X hi alone) ----------------------------------------------------
+
+def test_k_one_term_against_exact_rationals():
+    # ordinary blocks and blocks whose halves are 2^11 .. 2^15 apart (subnormal E4M3 terms)
+    xv, s = _cache_blocks(46, 40, 6)
+    rng = np.random.default_rng(47)
+    x = rng.standard_normal((40, 32))
+    x[:, :16] *= 400.0
+    x[:, 16:] *= np.exp2(-rng.uniform(2, 6, (40, 1)))
+    codes, sc = codec.quantize(x.astype(np.float32))
+    xv = np.concatenate([xv, codec.dequantize(codec.pack(codes), sc)])
+    s = np.concatenate([s, codec.e4m3_value(sc)])
+    got = a4q.k_one_term(xv, s)
+    for i in range(xv.shape[0]):
+        assert list(got[i]) == _bridge_brute(xv[i], s[i], terms=1), i
+    assert not np.array_equal(got, xv)
+
+
+def test_k_one_term_error_bound():
+    """|X hi - x| <= 2^-4 |x| in E4M3's normal range (|y| >= 2^-6) and <= 2^-10 X below it: half
+    a unit in the last place of a 3-bit mantissa, or of the subnormal step 2^-9."""
+    xv, s = _cache_blocks(48, 20000, 12)
+    _, _, e, _ = a4q.k_bridge(xv, s)
+    X = np.repeat(np.exp2(e), 32, axis=-1)
+    err = np.abs(a4q.k_one_term(xv, s) - xv)
+    normal = np.abs(xv / X) >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(xv[normal]))
+    assert np.all(err[~normal] <= 2.0 ** -10 * X[~normal])
+    assert err.max() > 0 and (~normal).any()
+
+
+def test_k_one_term_exact_for_power_of_two_scales_within_2_to_the_13():
+    """Both halves' scales powers of two at most 2^13 apart: X e2m1 2^k values with at most 2
+    significant bits, all inside E4M3's range, so X hi is the cache value itself."""
+    rng = np.random.default_rng(49)
+    n = 4000
+    a0 = rng.integers(-9, 9, n)
+    a1 = np.clip(a0 - rng.integers(0, 14, n), -9, 8)
+    codes = rng.integers(0, 16, (n, 32)).astype(np.uint8)
+    sv = np.stack([np.exp2(a0), np.exp2(a1)], axis=1).astype(np.float64)
+    xv = codec.e2m1_value(codes) * np.repeat(sv, 16, axis=-1)
+    assert np.array_equal(a4q.k_one_term(xv, sv), xv)
+    # one step past the bound the smallest values fall off E4M3's subnormal grid
+    sv2 = np.stack([np.full(n, 2.0 ** 5), np.full(n, 2.0 ** -9)], axis=1)
+    xv2 = codec.e2m1_value(codes) * np.repeat(sv2, 16, axis=-1)
+    assert not np.array_equal(a4q.k_one_term(xv2, sv2), xv2)
+
+
+def test_pins_catch_k_one_term_rounded_toward_zero():
+    def bad(x, s):  # E4M3 of y truncated instead of nearest-even
+        _, _, e, _ = a4q.k_bridge(x, s)
+        X = np.repeat(np.exp2(e), 32, axis=-1)
+        y = x / X
+        m, ex = np.frexp(np.abs(y))
+        step = np.ldexp(1.0, np.maximum(ex - 4, -9))
+        return np.sign(y) * np.floor(np.abs(y) / step) * step * X
+    xv, s = _cache_blocks(50, 40, 6)
+    with pytest.raises(AssertionError):
+        got = bad(xv, s)
+        for i in range(xv.shape[0]):
+            assert list(got[i]) == _bridge_brute(xv[i], s[i], terms=1), i
+
+
+def check_prefill_mx_paged(prefill_mx, q_format, seed=27, k_terms=2):
     """prefill_mx on a paged, ragged, GQA, causal batch against Python loops: queries quantized
-    by the exhaustive MX searches above, K bridged by exact rationals from independently
-    quantized values, softmax and PV in Python floats."""
+    by the exhaustive MX searches above, K bridged (k_terms 2) or rounded to its one-term form
+    (1) by exact rationals from independently quantized values, softmax and PV in Python
+    floats."""
     rng = np.random.default_rng(seed)
     d, hq, hkv, ps = 64, 4, 2, 16
     q_lens, kv_lens = [3, 1, 4], [19, 5, 33]
@@ -414,13 +479,14 @@ def check_prefill_mx_paged(prefill_mx, q_format, seed=27):
                     scs.append(float(table[sc]))
                     vals += [float((-1 if c & 8 else 1) * GRID[c & 7] * table[sc]) for c in codes]
                 for j in range(0, d, 32):
-                    kk[t, h, j:j + 32] = _bridge_brute(vals[j:j + 32], scs[j // 16:j // 16 + 2])
+                    kk[t, h, j:j + 32] = _bridge_brute(vals[j:j + 32], scs[j // 16:j // 16 + 2],
+                                                       terms=k_terms)
         kd.append(kk)
         vd.append(np.array([_nvfp4_row_brute(pins.bf16_value(r)) for r in vb.reshape(-1, d)]).reshape(kl, hkv, d))
         qs.append((rng.standard_normal((ql, hq, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
     qb = np.concatenate(qs)
     cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
-    got = prefill_mx(oc, qb, cu, kv_lens, bt, sm, q_format)
+    got = prefill_mx(oc, qb, cu, kv_lens, bt, sm, q_format, k_terms=k_terms)
     quant = _mx8_block_brute if q_format == "mxfp8" else _mx_block_brute
     for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
         for h in range(hq):
@@ -438,13 +504,21 @@ def check_prefill_mx_paged(prefill_mx, q_format, seed=27):
                     assert abs(got[cu[b] + i, h, t] - ref) < 1e-12, (q_format, b, h, i, t)
 
 
+@pytest.mark.parametrize("k_terms", [2, 1])
 @pytest.mark.parametrize("q_format", ["mxfp8", "mxfp4"])
-def test_prefill_mx_paged_ragged_vs_brute_force(q_format):
-    check_prefill_mx_paged(a4q.prefill_mx, q_format)
+def test_prefill_mx_paged_ragged_vs_brute_force(q_format, k_terms):
+    check_prefill_mx_paged(a4q.prefill_mx, q_format, k_terms=k_terms)
+
+
+def test_pins_catch_prefill_mx_one_term_with_the_bridged_k():
+    def bad(oc, qb, cu, kv_lens, bt, sm, q_format, k_terms):  # k_terms ignored: exact K
+        return a4q.prefill_mx(oc, qb, cu, kv_lens, bt, sm, q_format)
+    with pytest.raises(AssertionError):
+        check_prefill_mx_paged(bad, "mxfp8", k_terms=1)
 
 
 def test_pins_catch_prefill_mx_with_unbridged_queries():
-    def bad(oc, qb, cu, kv_lens, bt, sm, q_format):  # queries left unquantized
+    def bad(oc, qb, cu, kv_lens, bt, sm, q_format, k_terms=2):  # queries left unquantized
         from oracle import attention
         return attention.prefill(oc, qb, cu, kv_lens, bt, sm)[0]
     with pytest.raises(AssertionError):
