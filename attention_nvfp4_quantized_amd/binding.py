@@ -252,6 +252,7 @@ def prefill(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor,
 
 
 _A4Q_FORMATS = {"mxfp8": 0, "mxfp4": 1}
+_A4Q_K_ONE_TERM = 0x10
 
 
 def prefill_a4q_workspace_size(batch, total_q, max_q_len, max_kv_len, num_qo_heads, num_kv_heads,
@@ -264,11 +265,15 @@ def prefill_a4q(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor
                 kv_lens: torch.Tensor, block_table: torch.Tensor, max_q_len: int, max_kv_len: int,
                 sm_scale: float, q_format: str = "mxfp8", causal: bool = True,
                 out: torch.Tensor | None = None, out_dtype=torch.bfloat16, return_lse: bool = False,
-                num_splits: int = 0, workspace: torch.Tensor | None = None):
+                num_splits: int = 0, workspace: torch.Tensor | None = None, k_terms: int = 2):
     """paged_prefill_nvfp4_a4q: ``prefill`` with the query quantized in the kernel to MX blocks
-    (q_format "mxfp8" or "mxfp4") and QK on gfx950's block-scaled MFMA; NVFP4 caches only."""
+    (q_format "mxfp8" or "mxfp4") and QK on gfx950's block-scaled MFMA; NVFP4 caches only.
+    k_terms 2 feeds K exactly (two E4M3 terms), 1 its one-term form (K rounded to one E4M3 term
+    per value: half the QK matrix-core work)."""
     if q_format not in _A4Q_FORMATS:
         raise ValueError(f"q_format must be one of {sorted(_A4Q_FORMATS)}, got {q_format!r}")
+    if k_terms not in (1, 2):
+        raise ValueError(f"k_terms must be 1 or 2, got {k_terms!r}")
     odt = _attn_out_code(out_dtype if out is None else out.dtype)
     _need(q, torch.bfloat16, "q"); _need(cu_seqlens_q, torch.int32, "cu_seqlens_q")
     _need(kv_lens, torch.int32, "kv_lens"); _need(block_table, torch.int32, "block_table")
@@ -293,7 +298,8 @@ def prefill_a4q(cache: NVFP4KVCache, q: torch.Tensor, cu_seqlens_q: torch.Tensor
     _check(load_library().paged_prefill_nvfp4_a4q(
         ctypes.byref(d), q.data_ptr(), cu_seqlens_q.data_ptr(), kv_lens.data_ptr(),
         block_table.data_ptr(), block_table.shape[1], batch, total_q, max_q_len, max_kv_len, hq,
-        sm_scale, 1 if causal else 0, out.data_ptr(), odt, _ptr(lse), _A4Q_FORMATS[q_format],
+        sm_scale, 1 if causal else 0, out.data_ptr(), odt, _ptr(lse),
+        _A4Q_FORMATS[q_format] | (_A4Q_K_ONE_TERM if k_terms == 1 else 0),
         num_splits, _ptr(workspace) if ws_bytes else None, ws_bytes, _stream()))
     return (out, lse) if return_lse else out
 

@@ -263,7 +263,9 @@ int launch_prefill_plan(PrefillPlan& plan, void* workspace, size_t workspace_byt
                         hipStream_t st) {
   nvfp4kv::PrefillParams& p = plan.p;
   auto launch = [&]() {
-    if (q_format >= 0) return nvfp4kv::launch_prefill_a4q(p, q_format, st);
+    if (q_format >= 0)
+      return nvfp4kv::launch_prefill_a4q(p, q_format & ~NVFP4KV_A4Q_K_ONE_TERM,
+                                         (q_format & NVFP4KV_A4Q_K_ONE_TERM) ? 1 : 2, st);
     return plan.ncb ? nvfp4kv::launch_prefill_tail(p, plan.ncb, st) : nvfp4kv::launch_prefill(p, plan.nw, st);
   };
   if (p.num_splits > 1 || plan.ncb) {
@@ -518,7 +520,8 @@ int paged_prefill_nvfp4_a4q(const nvfp4kv_cache_t* cache, const void* q,
                             int32_t num_qo_heads, float sm_scale, int32_t causal, void* out,
                             int32_t out_dtype, float* lse, int32_t q_format, int32_t num_splits,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  if (q_format != NVFP4KV_A4Q_MXFP8 && q_format != NVFP4KV_A4Q_MXFP4)
+  const int q_base = q_format & ~NVFP4KV_A4Q_K_ONE_TERM;
+  if (q_base != NVFP4KV_A4Q_MXFP8 && q_base != NVFP4KV_A4Q_MXFP4)
     return fail(NVFP4KV_EINVAL, "q_format %d unknown", q_format);
   if (int e = check_cache(cache)) return e;
   if (cache->kv_format != NVFP4KV_FORMAT_NVFP4)

@@ -127,8 +127,9 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 hipError_t launch_repack(const RepackParams& p, int batch, int max_pages, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int waves, hipStream_t stream);
-// A4Q-style prefill (8-wave kernel; NVFP4 cache only); q_format 0 = MXFP8, 1 = MXFP4 queries.
-hipError_t launch_prefill_a4q(const PrefillParams& p, int q_format, hipStream_t stream);
+// A4Q-style prefill (8-wave kernel; NVFP4 cache only); q_format 0 = MXFP8, 1 = MXFP4 queries;
+// k_terms 2 = K as its exact two-term E4M3 bridge, 1 = the one-term (hi only) form.
+hipError_t launch_prefill_a4q(const PrefillParams& p, int q_format, int k_terms, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 // Short-query prefill (up to 64 query columns per sequence and KV head; p.chunk keys per slice,
 // at most 8192, or 2048 for ncb 4): ncb 1 or 2 column blocks of 16 per wavefront on key

@@ -20,6 +20,10 @@
 //  * QK is then two FP8 MFMAs per 32 keys x 32 columns x 64 head-dim values: the same matrix-core
 //    time as the stock fp16 path, with more conversion work per tile.  The bridge is what gfx950
 //    needs for an exact K; the A4Q saving of the pages' hardware does not carry over.
+//  * The one-term form (template argument KT = 1) keeps hi alone: one FP8 MFMA per 64 values, half
+//    the QK matrix-core time, at the cost of K rounded to E4M3's 4 significant bits under the
+//    block's power-of-two scale (relative error at most 2^-4 per value in E4M3's normal range):
+//    an approximation beyond the pages' A4Q, whose product takes K exactly.
 //
 // Operand layout of the 32x32x64 block-scaled MFMA (measured on the device): for lane l = r + 32h,
 // an FP8 operand holds reduction index k = 16h + i in bytes i = 0..15 and k = 32 + 16h + (i - 16)
@@ -152,7 +156,9 @@ __device__ __forceinline__ float load_q_mx(const PrefillParams& p, const Prefill
 }
 
 // Dequantize the loaded chunks into an A4Q tile buffer: V chunks to the fp16 V tile (as the stock
-// kernel), K chunks to their hi / lo E4M3 bytes and the E8M0 code of their 32-value block.
+// kernel), K chunks to their hi (and for KT = 2 lo) E4M3 bytes and the E8M0 code of their 32-value
+// block.
+template <int KT>
 __device__ __forceinline__ void store_tile_a4q(char* buf, const TileRegs<8, kFmtNvfp4>& r) {
   const int it = threadIdx.x;  // one chunk per thread and tile
   const bool is_v = (it >> 8) != 0;
@@ -191,6 +197,7 @@ __device__ __forceinline__ void store_tile_a4q(char* buf, const TileRegs<8, kFmt
     s16x2 t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(s16x2{0, 0}, ya, 1.0f, false);
     t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(t, yb, 1.0f, true);
     hi[i] = __builtin_bit_cast(uint32_t, t);
+    if constexpr (KT == 1) continue;
     // y - hi is exact in fp16: y has at most 6 significant bits and hi is y rounded to 4
     const f16x2 la = ya - __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi[i], 1.0f, false);
     const f16x2 lb = yb - __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi[i], 1.0f, true);
@@ -201,14 +208,16 @@ __device__ __forceinline__ void store_tile_a4q(char* buf, const TileRegs<8, kFmt
   char* row = buf + key * kQKStride + 32 * qq;
   *(u32x4*)(row) = u32x4{hi[0], hi[1], hi[2], hi[3]};
   *(u32x4*)(row + 16) = u32x4{hi[4], hi[5], hi[6], hi[7]};
-  *(u32x4*)(row + kQKPlane) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-  *(u32x4*)(row + kQKPlane + 16) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+  if constexpr (KT == 2) {
+    *(u32x4*)(row + kQKPlane) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    *(u32x4*)(row + kQKPlane + 16) = u32x4{lo[4], lo[5], lo[6], lo[7]};
+  }
   *(uint8_t*)(buf + kQScaleOff + 4 * key + qq) = (uint8_t)(E + 122);  // E8M0 code of 2^(E - 5)
 }
 
-// S^T (64 keys x this wave's 32 columns) from the hi and lo planes: per 32-key block and 64-value
-// k-step, one block-scaled MFMA for each plane (same E8M0 scale).
-template <int QF>
+// S^T (64 keys x this wave's 32 columns) from the hi and (KT = 2) lo planes: per 32-key block and
+// 64-value k-step, one block-scaled MFMA for each plane (same E8M0 scale).
+template <int QF, int KT>
 __device__ __forceinline__ void tile_scores_a4q(const char* buf, int lane, const i32x8 (&qb)[2],
                                                 const int (&qsc)[2], f32x16& s0, f32x16& s1) {
   const int r = lane & 31, h = lane >> 5;
@@ -219,11 +228,11 @@ __device__ __forceinline__ void tile_scores_a4q(const char* buf, int lane, const
   const uint32_t e1 = *(const uint32_t*)(buf + kQScaleOff + 4 * (32 + r));
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    i32x8 a[2][2];  // [key block][plane]
+    i32x8 a[2][KT];  // [key block][plane]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) {
+      for (int pl = 0; pl < KT; ++pl) {
         const char* src = buf + pl * kQKPlane + (32 * kb + r) * kQKStride + 64 * ks + 16 * h;
         const u32x4 x0 = *(const u32x4*)(src);
         const u32x4 x1 = *(const u32x4*)(src + 32);
@@ -234,13 +243,15 @@ __device__ __forceinline__ void tile_scores_a4q(const char* buf, int lane, const
     const int sk1 = (e1 >> (8 * (2 * ks + h))) & 0xFF;
     s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][0], qb[ks], s0, 0, kBFmt, 0, sk0, 0, qsc[ks]);
     s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][0], qb[ks], s1, 0, kBFmt, 0, sk1, 0, qsc[ks]);
-    s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], qb[ks], s0, 0, kBFmt, 0, sk0, 0, qsc[ks]);
-    s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], qb[ks], s1, 0, kBFmt, 0, sk1, 0, qsc[ks]);
+    if constexpr (KT == 2) {
+      s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], qb[ks], s0, 0, kBFmt, 0, sk0, 0, qsc[ks]);
+      s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], qb[ks], s1, 0, kBFmt, 0, sk1, 0, qsc[ks]);
+    }
   }
 }
 
 // The staggered 8-wave kernel of the stock path with A4Q tile buffers and scores.
-template <int QF>
+template <int QF, int KT>
 __global__ __launch_bounds__(512) void nvfp4_prefill_a4q_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[3 * kQBufBytes];
   PrefillItem w;
@@ -272,35 +283,35 @@ __global__ __launch_bounds__(512) void nvfp4_prefill_a4q_kernel(PrefillParams p)
   if (has_tiles) {
     load_tile<8, kFmtNvfp4>(p, bt_row, w.hk, w.kv_len, t0, min(t0 + 2, t_last), vzero, ra);
     load_tile<8, kFmtNvfp4>(p, bt_row, w.hk, w.kv_len, min(t0 + 1, t_last), min(t0 + 3, t_last), vzero, rb);
-    store_tile_a4q(smem, ra);
-    store_tile_a4q(smem + kQBufBytes, rb);
+    store_tile_a4q<KT>(smem, ra);
+    store_tile_a4q<KT>(smem + kQBufBytes, rb);
     __syncthreads();
     load_tile<8, kFmtNvfp4>(p, bt_row, w.hk, w.kv_len, min(t0 + 2, t_last), min(t0 + 4, t_last), vzero, ra);
     load_tile<8, kFmtNvfp4>(p, bt_row, w.hk, w.kv_len, min(t0 + 3, t_last), min(t0 + 5, t_last), vzero, rb);
 
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-    if (ahead && t0 * kTileKeys <= c.wlim_max) tile_scores_a4q<QF>(smem, lane, qb, qsc, s0, s1);
+    if (ahead && t0 * kTileKeys <= c.wlim_max) tile_scores_a4q<QF, KT>(smem, lane, qb, qsc, s0, s1);
     int bi = 0;  // buffer holding tile kt
-#define NVFP4KV_A4Q_STEP(KT, R)                                                                    \
+#define NVFP4KV_A4Q_STEP(TILE, R)                                                                  \
   {                                                                                                \
-    const int kt = (KT);                                                                           \
+    const int kt = (TILE);                                                                         \
     char* bcur = smem + bi * kQBufBytes;                                                           \
     char* bnext = smem + (bi == 2 ? 0 : bi + 1) * kQBufBytes;                                      \
     char* bfill = smem + (bi == 0 ? 2 : bi - 1) * kQBufBytes; /* receives tile kt+2 */             \
     const int k0 = kt * kTileKeys;                                                                 \
     if (k0 <= c.wlim_max) {                                                                        \
-      if (!ahead) tile_scores_a4q<QF>(bcur, lane, qb, qsc, s0, s1);                                \
+      if (!ahead) tile_scores_a4q<QF, KT>(bcur, lane, qb, qsc, s0, s1);                            \
       if (k0 + kTileKeys - 1 > c.wlim_min) tile_mask(s0, s1, k0, c.lim, c.h32);                    \
       tile_max_rescale(s0, s1, cs, m_used, l_part, acc_o);                                         \
       f16x8 pb[4];                                                                                 \
       tile_probs(s0, s1, cs, m_used, pb, l_part);                                                  \
       tile_pv_at(bcur + kQVOff, lane, pb, acc_o);                                                  \
     }                                                                                              \
-    store_tile_a4q(bfill, R);                                                                      \
+    store_tile_a4q<KT>(bfill, R);                                                                  \
     load_tile<8, kFmtNvfp4>(p, bt_row, w.hk, w.kv_len, min(kt + 4, t_last), min(kt + 6, t_last),   \
                             vzero, R);                                                             \
     if (ahead && kt + 1 < w.t_end && k0 + kTileKeys <= c.wlim_max)                                 \
-      tile_scores_a4q<QF>(bnext, lane, qb, qsc, s0, s1);                                           \
+      tile_scores_a4q<QF, KT>(bnext, lane, qb, qsc, s0, s1);                                       \
     __syncthreads();                                                                               \
     bi = bi == 2 ? 0 : bi + 1;                                                                     \
   }
@@ -315,12 +326,14 @@ __global__ __launch_bounds__(512) void nvfp4_prefill_a4q_kernel(PrefillParams p)
   prefill_epilogue(p, w, c, acc_o, m_used, l_part);
 }
 
-hipError_t launch_prefill_a4q(const PrefillParams& p, int q_format, hipStream_t stream) {
+hipError_t launch_prefill_a4q(const PrefillParams& p, int q_format, int k_terms, hipStream_t stream) {
   const dim3 grid((unsigned)(8 * p.items_per_xcd));
-  if (p.format != kFmtNvfp4) return hipErrorInvalidValue;
-  switch (q_format) {
-    case 0: hipLaunchKernelGGL(nvfp4_prefill_a4q_kernel<kQfMxfp8>, grid, dim3(512), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL(nvfp4_prefill_a4q_kernel<kQfMxfp4>, grid, dim3(512), 0, stream, p); break;
+  if (p.format != kFmtNvfp4 || (k_terms != 1 && k_terms != 2)) return hipErrorInvalidValue;
+  switch (2 * q_format + k_terms - 1) {
+    case 0: hipLaunchKernelGGL((nvfp4_prefill_a4q_kernel<kQfMxfp8, 1>), grid, dim3(512), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((nvfp4_prefill_a4q_kernel<kQfMxfp8, 2>), grid, dim3(512), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((nvfp4_prefill_a4q_kernel<kQfMxfp4, 1>), grid, dim3(512), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((nvfp4_prefill_a4q_kernel<kQfMxfp4, 2>), grid, dim3(512), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -397,9 +397,10 @@ def _blas_threads():
 
 def run_a4q(name, torch, A, reps=20):
     """The A4Q-style prefill (query quantized to MX blocks in the kernel, QK on the block-scaled
-    MFMA; MXFP8 and MXFP4 queries) against the stock prefill on the same cache: median µs per
-    call, with a 512 MB buffer read before each call for the short shape (cold caches) and
-    back to back for the full one."""
+    MFMA; MXFP8 and MXFP4 queries; K exact as two E4M3 terms, or as one term with the "_k1"
+    suffix) against the stock prefill on the same cache: median µs per call, with a 512 MB
+    buffer read before each call for the short shape (cold caches) and back to back for the
+    full one."""
     pc = prefill_case(name)
     w = pc.w
     cache = A.NVFP4KVCache(pc.layout.num_pages, w.num_kv_heads)
@@ -423,6 +424,12 @@ def run_a4q(name, torch, A, reps=20):
                                            w.sm_scale, q_format="mxfp8", out=out, workspace=ws),
         "a4q_mxfp4": lambda: A.prefill_a4q(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len,
                                            w.sm_scale, q_format="mxfp4", out=out, workspace=ws),
+        "a4q_mxfp8_k1": lambda: A.prefill_a4q(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len,
+                                              w.sm_scale, q_format="mxfp8", out=out, workspace=ws,
+                                              k_terms=1),
+        "a4q_mxfp4_k1": lambda: A.prefill_a4q(cache, q, cu, kv, bt, pc.max_q_len, pc.max_kv_len,
+                                              w.sm_scale, q_format="mxfp4", out=out, workspace=ws,
+                                              k_terms=1),
     }
     res = {"workload": name, "mode": "flushed" if flush is not None else "warm"}
     for key, fn in calls.items():
@@ -436,10 +443,11 @@ def run_a4q(name, torch, A, reps=20):
             e[1].record()
         torch.cuda.synchronize()
         res["us_" + key] = round(float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3, 2)
-    for key in ("a4q_mxfp8", "a4q_mxfp4"):
+    for key in ("a4q_mxfp8", "a4q_mxfp4", "a4q_mxfp8_k1", "a4q_mxfp4_k1"):
         res["ratio_" + key + "_over_stock"] = round(res["us_" + key] / res["us_stock"], 3)
     flops = prefill_flops(w.q_lens, w.kv_lens, w.num_qo_heads)
-    res["TFLOPs_a4q_mxfp8"] = round(flops / (res["us_a4q_mxfp8"] * 1e-6) / 1e12, 2)
+    for key in ("a4q_mxfp8", "a4q_mxfp8_k1"):
+        res["TFLOPs_" + key] = round(flops / (res["us_" + key] * 1e-6) / 1e12, 2)
     return res
 
 

@@ -273,6 +273,11 @@ def test_a4q_prefill_argument_checks():
                                            a["wsb"], None)
     d = _desc()
     assert call(d, qf=2) == -1 and "q_format" in _err()
+    assert call(d, qf=0x12) == -1 and "q_format" in _err()  # the one-term flag on no format
+    assert call(d, qf=0x20) == -1 and "q_format" in _err()
+    assert call(d, qf=0x11, total_q=0) == 0 and _err() == ""  # MXFP4 queries, one-term K
+    with pytest.raises(ValueError, match="k_terms"):
+        A.prefill_a4q(None, None, None, None, None, 1, 1, 1.0, k_terms=3)
     assert call(_desc(kv_format=1, k_scale=None, v_scale=None)) == -2 and "NVFP4" in _err()
     assert call(d, hq=30) == -1 and "multiple" in _err()
     assert call(d, bts=2) == -1 and "block_table_stride" in _err()
