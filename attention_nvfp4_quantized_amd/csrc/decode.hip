@@ -55,7 +55,7 @@ __device__ __forceinline__ int page_at(int pt0, int pt1, int pi) {
 // Issue the loads of the 32 tokens starting at k (two 16-token groups, one page each).  Loads
 // are unconditional: a group past the wave's range re-reads the range's last group (an L2 hit),
 // and tokens past the range are zeroed at use time, so every step issues the same 8 loads and
-// the wait counts stay exact.  Every cache byte is read once per call, so the loads are
+// the wait counts stay exact.  Every cache byte is read once per call, so the NVFP4 loads are
 // non-temporal (streaming): measured 340 -> 320 us per call of the decode workload, and a plain
 // streaming-read kernel reaches 6.1 TB/s with such loads against 5.4 TB/s without.
 template <int FMT>
@@ -77,10 +77,12 @@ __device__ __forceinline__ void decode_load(const DecodeParams& p, int hk, int w
     } else {
       const uint8_t* kp = p.k_data + row * kHeadDim + 32 * q4;
       const uint8_t* vp = p.v_data + row * kHeadDim + 32 * q4;
-      r.kd[g] = __builtin_nontemporal_load((const u32x4*)kp);
-      r.kd2[g] = __builtin_nontemporal_load((const u32x4*)(kp + 16));
-      r.vd[g] = __builtin_nontemporal_load((const u32x4*)vp);
-      r.vd2[g] = __builtin_nontemporal_load((const u32x4*)(vp + 16));
+      // ordinary loads: each instruction covers every other 16 bytes of the rows, and as
+      // streaming loads the second instruction fetched the lines again (FP8 decode 560 -> 720 us)
+      r.kd[g] = *(const u32x4*)kp;
+      r.kd2[g] = *(const u32x4*)(kp + 16);
+      r.vd[g] = *(const u32x4*)vp;
+      r.vd2[g] = *(const u32x4*)(vp + 16);
     }
   }
 }

@@ -56,7 +56,7 @@ __device__ __forceinline__ int tail_page(int pt0, int pt1, int pi) {
 
 // Loads of one plane for the 32 keys starting at k, unconditional: a group past the quarter's
 // range re-reads its last group (an empty range reads its first page), and keys past the range
-// are zeroed at use.  Each cache byte is read by one workgroup once, so the loads are
+// are zeroed at use.  Each cache byte is read by one workgroup once, so the NVFP4 loads are
 // non-temporal (streaming).
 template <int FMT>
 __device__ __forceinline__ void plane_load(const PrefillParams& p, const uint8_t* data,
@@ -74,8 +74,8 @@ __device__ __forceinline__ void plane_load(const PrefillParams& p, const uint8_t
       r.s[g] = __builtin_nontemporal_load((const uint32_t*)(scale + row * kScaleBytes + 4 * (q4 >> 1)));
     } else {
       const uint8_t* dp = data + row * kHeadDim + 32 * q4;
-      r.d[g] = __builtin_nontemporal_load((const u32x4*)dp);
-      r.d2[g] = __builtin_nontemporal_load((const u32x4*)(dp + 16));
+      r.d[g] = *(const u32x4*)dp;  // ordinary loads: see group_load
+      r.d2[g] = *(const u32x4*)(dp + 16);
     }
   }
 }
@@ -460,8 +460,10 @@ __device__ __forceinline__ void group_load(const PrefillParams& p, const uint8_t
     r.s = __builtin_nontemporal_load((const uint32_t*)(scale + row * kScaleBytes + 4 * (q4 >> 1)));
   } else {
     const uint8_t* dp = data + row * kHeadDim + 32 * q4;
-    r.d = __builtin_nontemporal_load((const u32x4*)dp);
-    r.d2[0] = __builtin_nontemporal_load((const u32x4*)(dp + 16));
+    // ordinary loads: each instruction covers every other 16 bytes of the rows, and as
+    // streaming loads the second instruction would fetch the lines again
+    r.d = *(const u32x4*)dp;
+    r.d2[0] = *(const u32x4*)(dp + 16);
   }
 }
 
