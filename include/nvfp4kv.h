@@ -191,12 +191,11 @@ int paged_prefill_nvfp4(const nvfp4kv_cache_t* cache, const void* q, const int32
  * per 32 values (exact when a key's two 16-value block scales in each 32-value block are within
  * 2^8 of each other); softmax and PV are those of paged_prefill_nvfp4.  NVFP4 caches only
  * (other formats: NVFP4KV_EUNSUPPORTED).  Every query-tile width runs the 8-wave kernel.
- *             OR-ing NVFP4KV_A4Q_K_ONE_TERM into q_format keeps the first term alone: one MFMA
- *             instead of two per 64 head-dim values, K rounded to nearest-even E4M3 (4
- *             significant bits) under the block's power-of-two scale, relative error at most
- *             2^-4 per value where the value is at least 2^-6 times that scale.  This is an extra
- *             approximation: the pages' A4Q product takes K exactly.  Any other q_format:
- *             NVFP4KV_EINVAL.
+ * OR-ing NVFP4KV_A4Q_K_ONE_TERM into q_format keeps the first term alone: one MFMA instead of
+ * two per 64 head-dim values, K rounded to nearest-even E4M3 (4 significant bits) under the
+ * block's power-of-two scale, relative error at most 2^-4 per value where the value is at least
+ * 2^-6 times that scale.  This is an extra approximation: the pages' A4Q product takes K
+ * exactly.  Any other q_format: NVFP4KV_EINVAL.
  */
 #define NVFP4KV_A4Q_MXFP8 0
 #define NVFP4KV_A4Q_MXFP4 1
